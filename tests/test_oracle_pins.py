@@ -1,0 +1,102 @@
+"""CPU tests: the oracle against its pins, planted-mistake detection, the 16-token bound."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins
+from tests.chunked_ref import affine_map
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(oracle_lib, pin):
+    pin(oracle_lib)
+
+
+# Each planted mistake (compiled into a separate copy of the oracle) must be caught by at
+# least one pin: a dropped or misplaced term, a wrong sign, a transposed decay, a wrong
+# gate, a wrong cumsum -- so a pin set that passes is evidence, not a tautology.
+MUTANTS = {
+    1: "decay columns instead of rows",
+    2: "decay after the edit",
+    3: "read before the write",
+    4: "erase not scaled by beta",
+    5: "sign of the write",
+    6: "e^A replaced by A in the gate",
+    7: "Sigmoid(-x) in the gate",
+    8: "exclusive chunk cumsum",
+    9: "chunks aligned to the packed batch, not the sequence",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m])
+def test_planted_mistake_is_caught(tmp_path, mutant):
+    path = oracle.build(str(tmp_path / f"libkda_oracle_m{mutant}.so"), mutant=mutant)
+    orc = oracle.Oracle(path)
+    assert orc.mutant == mutant
+    bad = oracle_pins.failing_pins(orc)
+    assert bad, f"mutant {mutant} ({MUTANTS[mutant]}) passed every pin"
+
+
+# --- the 16-token tile bound ("Kimi K3: Architecture, ..." §3.3; "Kimi K3 Under the Hood",
+# sequence-mixing section): with g >= -5 a 16-token tile's cumulative log-decay stays in
+# [-80, 0], so e^{+-80} factors are finite normal numbers in bf16/fp32. ----------------------
+
+BF16_MAX = 3.3895313892515355e38
+FP32_MIN_NORMAL = 1.1754943508222875e-38
+
+
+def _config_gates(orc, z_mean, seed, T=4096, H=4, d=128):
+    rng = np.random.default_rng(seed)
+    z = rng.normal(z_mean, 1.0, (T, H, d)).astype(np.float32)
+    A = rng.normal(0.0, 0.5, (H, d)).astype(np.float32)
+    return z, A, orc.gate(z, A)
+
+
+@pytest.mark.parametrize("z_mean", [0.0, 6.0, -4.0])
+def test_sixteen_token_tile_bound(oracle_lib, z_mean):
+    z, A, g = _config_gates(oracle_lib, z_mean, seed=30)
+    G16 = oracle_lib.chunk_cumsum(g, None, chunk=16)
+    assert G16.min() >= -80.0 and G16.max() <= 0.0
+    tile_sums = G16[15::16]
+    assert tile_sums.min() >= -80.0
+    # the reciprocal factor e^{-Gamma} and the forward factor e^{Gamma} stay finite, normal
+    assert math.exp(-G16.min()) < BF16_MAX
+    assert math.exp(G16.min()) > FP32_MIN_NORMAL
+
+
+def test_bound_negative_controls(oracle_lib):
+    """A single 64-token reference would overflow, and an unbounded gate breaks the
+    16-token bound: the tile structure and the lower bound are both needed."""
+    z, A, g = _config_gates(oracle_lib, 0.0, seed=31)
+    G64 = oracle_lib.chunk_cumsum(g, None, chunk=64)
+    assert G64.min() < -math.log(np.finfo(np.float32).max)  # e^{-Gamma_64} overflows fp32
+    # unbounded gate of the earlier design: negative softplus of the same logits
+    x = np.exp(A.astype(np.float64))[None] * z.astype(np.float64) + 6.0
+    g_unb = -np.logaddexp(0.0, x)
+    G16u = oracle_lib.chunk_cumsum(g_unb, None, chunk=16)
+    assert G16u.min() < -80.0
+
+
+def test_chunk_affine_map_matches_explicit_product():
+    """The per-chunk affine transition S_out = M S_in + b equals the explicit product
+    prod_t (I - beta_t k_t k_t^T) Diag(alpha_t) (the context-parallel fragment)."""
+    rng = np.random.default_rng(32)
+    n, dk, dv = 24, 8, 6
+    k = rng.standard_normal((n, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    beta = rng.uniform(0, 1, n)
+    g = rng.uniform(-5, 0, (n, dk))
+    v = rng.standard_normal((n, dv))
+    M, b = affine_map(k, beta, g, v)
+    P = np.eye(dk)
+    bb = np.zeros((dk, dv))
+    for t in range(n):
+        Mt = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(g[t]))
+        P = Mt @ P
+        bb = Mt @ bb + beta[t] * np.outer(k[t], v[t])
+    assert np.max(np.abs(M - P)) < 1e-12
+    assert np.max(np.abs(b - bb)) < 1e-12
