@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one kda_prefill_fwd call over the named prefill workload (gate, intra-chunk
+products, triangular solve, state pass and outputs all run inside it).  The same line also
+carries the decode half of the metric: 256 consecutive kda_decode_step calls over
+512 sequences x 32 heads.  Inputs are seeded synthetic data resident in HBM before timing.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + MFMA util; decode tokens/s + HBM GB/s"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+CHUNK = 64
+
+
+def prefill_algorithmic(dk: int, dv: int, elem: int, z_bytes: int = 4):
+    """Algorithmic work of the chunkwise prefill per token-head at chunk C = 64 (what the
+    method must compute and move; masked, recomputed or dense-padding work excluded):
+      flops: per chunk 6 C dk dv (the three state products) + C(C-1) dk (A_kk, strictly
+             lower) + 2 C(C+1) dk (A_qk, and W = T K, lower incl.) + 2 C(C+1) dv (T V and
+             A_qk U) + C^3/3 (the triangular inverse), divided by C
+      bytes: q, k, v, beta and o in the element type, z in fp32 (states amortised)."""
+    C = CHUNK
+    flops = (6 * C * dk * dv + C * (C - 1) * dk + 2 * C * (C + 1) * dk + 2 * C * (C + 1) * dv
+             + C ** 3 / 3) / C
+    byts = (2 * dk + dv) * elem + elem + z_bytes * dk + dv * elem
+    return flops, byts
+
+
+def decode_bytes_per_pair(dk: int, dv: int, elem: int):
+    """State read + write (fp32) plus one token's inputs and output."""
+    return 2 * dk * dv * 4 + prefill_algorithmic(dk, dv, elem)[1]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_sequence_chunkwise_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM traffic per launch measured by rocprofv3 counters, if a summary for the current
+    kernel sources exists under profiles/ (else None)."""
+    path = os.path.join(ROOT, "profiles", f"prefill_chain_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, budget_s: float = 20.0):
+    """The oracle, untuned, on the host cores over a bounded sample of the same workload:
+    whole (sequence, head) pairs are added until about budget_s of estimated CPU time."""
+    import oracle
+    orc = oracle.load()
+    threads = cpu_threads()
+    pairs = [(n, h) for n in range(inp.N) for h in range(inp.H)]
+    # a first pair measures the rate; then as many pairs as fit the budget (multiple of threads)
+    t0 = time.perf_counter()
+    _run_oracle_pairs(orc, inp, pairs[:1], 1)
+    one = time.perf_counter() - t0
+    per_round = max(one, 1e-4)
+    n_more = int(min(len(pairs) - 1, max(threads, (budget_s / per_round) * threads)))
+    n_more = max(0, (n_more // threads) * threads) if n_more >= threads else n_more
+    sample = pairs[1:1 + n_more] if n_more > 0 else pairs[:1]
+    t0 = time.perf_counter()
+    _run_oracle_pairs(orc, inp, sample, threads)
+    secs = time.perf_counter() - t0
+    tok_heads = sum(inp.lengths[n] for n, _ in sample)
+    tokens_per_s = tok_heads / secs / inp.H   # sequence tokens/s over all H heads
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} of {len(pairs)} (sequence, head) pairs of the same workload, "
+                      f"{tok_heads} token-heads in {secs:.2f} s; fp64 token recurrence"}
+
+
+def _run_oracle_pairs(orc, inp, pairs, threads):
+    f = lambda t: t.float().numpy()
+    # pass only the needed heads' data via per-pair slices to keep host memory bounded
+    by_head = {}
+    for n, h in pairs:
+        by_head.setdefault(h, []).append(n)
+    for h, ns in by_head.items():
+        sl = slice(h, h + 1)
+        orc.prefill(f(inp.q[:, sl]), f(inp.k[:, sl]), f(inp.v[:, sl]), f(inp.beta[:, sl]),
+                    z=inp.z[:, sl].numpy(), A=inp.A[sl].numpy(),
+                    S0=None if inp.S0 is None else inp.S0[:, sl].numpy(),
+                    cu_seqlens=inp.cu_seqlens.numpy(), pairs=[(n, 0) for n in ns],
+                    n_threads=threads, want_state=False)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MI355X: this build runs on a single GPU "
+              "(the (sequence, head) chains shard across GPUs with no communication; "
+              "multi-GPU runs are not part of it).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kda.load_library()
+    name = args.workload or workloads.PREFILL_B1
+    inp = workloads.make(name)
+    dev = lambda t: None if t is None else t.cuda()
+    q, k, v, beta, z, A = map(dev, (inp.q, inp.k, inp.v, inp.beta, inp.z, inp.A))
+    s0 = dev(inp.S0)
+    cu = None if inp.equal_length else dev(inp.cu_seqlens)
+    want_final = name in (workloads.PREFILL_B4, workloads.PREFILL_VARLEN)
+    sN = torch.empty((inp.N, inp.H, inp.dk, inp.dv), dtype=torch.float32, device="cuda") \
+        if want_final else None
+    o = torch.empty((inp.total, inp.H, inp.dv), dtype=q.dtype, device="cuda")
+
+    def step():
+        kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=sN,
+                            cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = ev0.elapsed_time(ev1) / args.steps  # average launch duration on this stream
+    ms_per_step = wall * 1e3 / args.steps
+
+    elem = 2 if inp.dtype == "bf16" else 4
+    fl, by = prefill_algorithmic(inp.dk, inp.dv, elem)
+    tok_heads = inp.total * inp.H
+    state_bytes = (0 if s0 is None else s0.numel() * 4) + (0 if sN is None else sN.numel() * 4)
+    alg_bytes = by * tok_heads + state_bytes
+    achieved = alg_bytes / (ms_event * 1e-3) / 1e9
+    traffic = read_traffic(name)
+    tokens_per_s = inp.total / (ms_per_step * 1e-3)
+    mfma_tflops = fl * tok_heads / (ms_event * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic, seeded (q,k ~N(0,1) L2-normalised per head, q/sqrt(dk); v ~N(0,1); "
+                "beta=Sigmoid(N(0,1)); z ~N(0,1); A ~N(0,0.5))",
+        "config": {"workload": name, "sequences": inp.N, "total_tokens": inp.total,
+                   "heads": inp.H, "dk": inp.dk, "dv": inp.dv, "chunk": CHUNK,
+                   "initial_state": s0 is not None, "final_state": sN is not None,
+                   "cache": "warm: back-to-back calls"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if traffic is None else traffic,
+                     "kernel": "prefill_chain_kernel", "avg_launch_ms": ms_event,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma_util": {"useful_tflops": mfma_tflops, "peak_tflops": BF16_PEAK_TFLOPS,
+                      "frac": mfma_tflops / BF16_PEAK_TFLOPS,
+                      "useful_flops_per_token_head": fl},
+    }
+
+    if not args.no_decode:
+        out["decode"] = bench_decode(args.decode_steps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(n_steps: int, distinct: int = 32, repeats: int = 3):
+    """256 consecutive decode steps (512 sequences x 32 heads, d = 128, bf16 inputs, fp32
+    state in place).  `distinct` step inputs are generated and cycled (each 21 MB, so a
+    cycle exceeds the 256 MB last-level cache); the state is restored between repeats
+    outside the timed region."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda, workloads
+    d = workloads.decode_inputs(N=512, H=32, dk=128, dv=128, steps=distinct, dtype="bf16",
+                                seed=4, name=workloads.DECODE)
+    q, k, v, beta, z = (t.cuda() for t in (d.q, d.k, d.v, d.beta, d.z))
+    A = d.A.cuda()
+    s_init = d.S0.cuda()
+    state = s_init.clone()
+    o = torch.empty((d.N, d.H, d.dv), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for t in range(n_steps):
+            j = t % distinct
+            kda.kda_decode_step(q[j], k[j], v[j], beta[j], z[j], A, state, o=o)
+
+    run()  # warm-up
+    times = []
+    for _ in range(repeats):
+        state.copy_(s_init)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.median(times))
+    per_step = t / n_steps
+    byts = decode_bytes_per_pair(d.dk, d.dv, 2) * d.N * d.H
+    gbps = byts / per_step / 1e9
+    return {"workload": workloads.DECODE, "steps": n_steps, "tokens_per_s": d.N * n_steps / t,
+            "us_per_step": per_step * 1e6, "hbm_GBps": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "decode_kernel", "algorithmic_bytes_per_launch": byts},
+            "inputs": f"{distinct} distinct seeded steps cycled"}
+
+
+if __name__ == "__main__":
+    main()

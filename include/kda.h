@@ -1,0 +1,152 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) forward pass.
+ *
+ * Sources, by page title and section:
+ *   [K3 note]  "Kimi K3: Architecture, Training, and Million-Token Agentic RL"
+ *              (Awesome-LLM-Research-Collections note on the K3 technical report)
+ *   [K3 hood]  "Kimi K3 Under the Hood: A 2.8T MoE Built for Million-Token Agents"
+ *
+ * The operator, per (sequence, head), with state S in R^{dk x dv} (rows = key channels):
+ *   g_t = g_min * Sigmoid(e^{A} z_t),  alpha_t = e^{g_t},  g_min = -5      [K3 note] §3.3
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T  [K3 note] §3.1
+ *   o_t = S_t^T q_t   (read after the update; no scale is applied to q)   [K3 note] §3.2
+ * Prefill evaluates it chunk by chunk (64-token chunks of 16-token tiles); decode advances
+ * the state by one token ([K3 note] §3.3, recurrent decoding and chunked prefill).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or keeps device memory, and keeps no state between calls.
+ *   - Layouts are row-major with the last dimension contiguous:
+ *       q, k, z  [tokens, H, dk]      v, o  [tokens, H, dv]      beta  [tokens, H]
+ *       A        [H, dk]              states [N, H, dk, dv] (dv fastest, rows = key channels)
+ *     q, k, v, beta and o have the element type given by `dt`; z, A and all states are fp32.
+ *   - Pointers must be 16-byte aligned, except beta (element-aligned) and cu_seqlens
+ *     (4-byte aligned); KDA_ERR_ALIGN otherwise.  Pointers to per-token
+ *     tensors (q, k, v, beta, z, g, gcum, o) may be NULL only when the call has no tokens
+ *     (then nothing is read or written through them); otherwise NULL is KDA_ERR_NULL.
+ *   - Work is enqueued on `stream` (NULL = the default stream); calls return before it
+ *     finishes.  Argument checks run on the host before anything is enqueued; on an error
+ *     nothing is launched and nothing is written.  Device-side faults surface at the
+ *     caller's next synchronisation.  The contents of cu_seqlens are not validated (that
+ *     would need a synchronisation): they must start at 0, be non-decreasing and end at
+ *     the token count.  NaN/Inf inputs propagate.
+ *   - Calls are thread-safe; calls that overlap on the same output memory race.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL                                 */
+    KDA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or too big  */
+    KDA_ERR_UNSUPPORTED = -3, /* head size, element type or g_min outside what is compiled  */
+    KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                           */
+    KDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kda_prefill_workspace_size */
+    KDA_ERR_HIP = -6          /* the HIP runtime rejected a launch                          */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0, /* q, k, v, beta, o are fp32 (contractions still run on bf16 MFMA)   */
+    KDA_BF16 = 1 /* q, k, v, beta, o are bf16; o is rounded to nearest even           */
+} kda_dtype;
+
+/* Largest chunk length accepted by kda_gate. */
+#define KDA_GATE_MAX_CHUNK 1024
+
+/*
+ * kda_gate -- lower-bounded decay gate and chunk-local cumulative log-decay.
+ * [K3 note] §3.3 (lower-bounded decay; reciprocal cumulative decay in chunked prefill);
+ * [K3 hood] "Sequence mixing" (the retention parameterisation).
+ *
+ *   g[t,h,c]    = g_min * Sigmoid(exp(A[h,c]) * z[t,h,c])          (fp32)
+ *   gcum[t,h,c] = sum of g[t',h,c] over t' from the start of t's chunk up to t inclusive
+ * Chunks are `chunk` tokens long and restart at every sequence start; a sequence's last
+ * chunk may be shorter.
+ *
+ *   z, A        input, fp32 ([total_tokens, H, dk], [H, dk])
+ *   g, gcum     outputs, fp32 [total_tokens, H, dk]; either may be NULL, not both
+ *   cu_seqlens  device int32 [n_seqs + 1] sequence starts, or NULL for n_seqs sequences of
+ *               total_tokens / n_seqs tokens each (then total_tokens % n_seqs must be 0)
+ *   chunk       1 .. KDA_GATE_MAX_CHUNK (the prefill uses 64)
+ *   g_min       finite and < 0 (the pages fix -5)
+ *   dk          a multiple of 4; total_tokens >= 0; H >= 1; n_seqs >= 1
+ */
+kda_status kda_gate(const float* z, const float* A, float* g, float* gcum,
+                    int64_t total_tokens, int H, int dk, const int32_t* cu_seqlens,
+                    int n_seqs, int chunk, float g_min, hipStream_t stream);
+
+/*
+ * kda_prefill_workspace_size -- bytes of device workspace kda_prefill_fwd needs for this
+ * problem (a multiple of 256; may be 0).  Returns 0 for invalid sizes as well; the
+ * prefill call reports those.
+ */
+size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
+                                  kda_dtype dt);
+
+/*
+ * kda_prefill_fwd -- chunkwise KDA prefill over a packed batch.
+ * [K3 note] §3.3 (chunked prefill: (X_[c], S_in) -> (Y_[c], S_out), S_in[c+1] = S_out[c];
+ * 16-token tiles whose cumulative log-decay stays in (-80, 0) so every tile, diagonal or
+ * not, is a dense bf16 matrix product); §3.1-§3.2 (the recurrence it evaluates);
+ * [K3 hood] "Serving two incompatible cache types" (a prefix hit restores the state at
+ * the hit boundary and resumes prefill from it; cached checkpoints are read-only).
+ *
+ *   dt             element type of q, k, v, beta and o
+ *   q, k           [total, H, dk];  v [total, H, dv];  beta [total, H]
+ *   z, A           decay logits [total, H, dk] and per-(head, channel) A [H, dk], fp32;
+ *                  the gate above is applied inside the kernel
+ *   g_min          in [-5, 0): the 16-token bound needs g >= -5 (KDA_ERR_UNSUPPORTED else)
+ *   initial_state  fp32 [N, H, dk, dv], read only, or NULL for zero states
+ *   final_state    fp32 [N, H, dk, dv] written with each sequence's last state, or NULL;
+ *                  may alias initial_state only as the very same pointer
+ *   cu_seqlens     device int32 [N + 1], or NULL for N sequences of T_or_total tokens each
+ *   n_seqs         N >= 1
+ *   T_or_total     tokens per sequence when cu_seqlens is NULL, else the packed total
+ *   dk, dv         64 or 128 each, dk == dv
+ *   o              [total, H, dv] output of type dt
+ *   workspace      device scratch of at least kda_prefill_workspace_size(...) bytes
+ *                  (may be NULL when that size is 0); contents on return are undefined
+ * A zero-length sequence writes no output rows and copies its initial state (or zeros) to
+ * final_state.  Results equal the token recurrence up to floating-point association.
+ */
+kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const void* v,
+                           const void* beta, const float* z, const float* A, float g_min,
+                           const float* initial_state, float* final_state,
+                           const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
+                           int dk, int dv, void* o, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * kda_decode_step -- one recurrent decode step for N sequences x H heads, state in place.
+ * [K3 note] §3.2 (the per-token map (x_t, S_{t-1}) -> (y_t, S_t) and its order: decay
+ * Sbar = Diag(alpha) S, predict vhat = Sbar^T k, write S = Sbar + beta k (v - vhat)^T,
+ * read o = S^T q after the write); §3.3 (recurrent decoding, one token at a time).
+ *
+ *   q, k, z        [N, H, dk] (one token per sequence);  v [N, H, dv];  beta [N, H]
+ *   A              [H, dk] fp32;  g_min finite and < 0
+ *   state          fp32 [N, H, dk, dv], read and overwritten with S_t
+ *   o              [N, H, dv] output of type dt
+ *   dk, dv         64 or 128 each, dk == dv
+ */
+kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const void* v,
+                           const void* beta, const float* z, const float* A, float g_min,
+                           float* state, int N, int H, int dk, int dv, void* o,
+                           hipStream_t stream);
+
+/* kda_status_str -- a static, human-readable name for a status code. */
+const char* kda_status_str(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,152 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument checks, then kernel launch.
+//
+// Every check runs on the host before any HIP call, so an invalid call launches nothing
+// and writes nothing.  The library allocates nothing and keeps no state between calls
+// except a per-device cache of the compute-unit count used to size launches.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kda_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// beta is read one element at a time: element alignment suffices.
+bool beta_aligned(const void* p, kda_dtype dt) {
+    return (reinterpret_cast<uintptr_t>(p) & (dt == KDA_BF16 ? 1u : 3u)) == 0;
+}
+
+bool supported_d(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // far beyond any device memory
+
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid or inconsistent size";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size, dtype or g_min not supported";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+    }
+    return "unknown kda_status";
+}
+
+kda_status kda_gate(const float* z, const float* A, float* g, float* gcum, int64_t total_tokens,
+                    int H, int dk, const int32_t* cu_seqlens, int n_seqs, int chunk, float g_min,
+                    hipStream_t stream) {
+    if (total_tokens < 0 || H <= 0 || dk <= 0 || n_seqs <= 0) return KDA_ERR_SHAPE;
+    if (!A || (total_tokens > 0 && (!z || (!g && !gcum)))) return KDA_ERR_NULL;
+    if (dk % 4 != 0) return KDA_ERR_UNSUPPORTED;
+    if (chunk < 1 || chunk > KDA_GATE_MAX_CHUNK) return KDA_ERR_SHAPE;
+    if (!std::isfinite(g_min) || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
+    if (!cu_seqlens && total_tokens % n_seqs != 0) return KDA_ERR_SHAPE;
+    if (total_tokens > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
+    if (static_cast<int64_t>(H) * dk / 4 > int64_t(65535) * 256) return KDA_ERR_SHAPE;
+    if ((total_tokens + chunk - 1) / chunk > int64_t(0x7fffffff)) return KDA_ERR_SHAPE;
+    if (!aligned16(z) || !aligned16(A) || (g && !aligned16(g)) || (gcum && !aligned16(gcum)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)))
+        return KDA_ERR_ALIGN;
+    if (total_tokens == 0) return KDA_OK;
+    kda::GateArgs a{};
+    a.z = z; a.A = A; a.g = g; a.gcum = gcum; a.total = total_tokens; a.H = H; a.dk = dk;
+    a.cu = cu_seqlens; a.n_seqs = n_seqs;
+    a.T = cu_seqlens ? 0 : total_tokens / n_seqs;
+    a.chunk = chunk; a.g_min = g_min;
+    return kda::launch_gate(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
+                                  kda_dtype dt) {
+    (void)total_tokens; (void)n_seqs; (void)H; (void)dk; (void)dv; (void)dt;
+    return 0;  // the fused chain kernel keeps every intermediate on chip
+}
+
+kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const void* v,
+                           const void* beta, const float* z, const float* A, float g_min,
+                           const float* initial_state, float* final_state,
+                           const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
+                           int dk, int dv, void* o, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (n_seqs <= 0 || T_or_total < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    const int64_t total = cu_seqlens ? T_or_total : static_cast<int64_t>(n_seqs) * T_or_total;
+    // per-token tensors may be NULL only when there are no tokens
+    if (!A || (total > 0 && (!q || !k || !v || !beta || !z || !o))) return KDA_ERR_NULL;
+    if (!supported_d(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(g_min) || g_min < -5.f || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
+    if (!cu_seqlens && n_seqs > 0 && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
+    if (total > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
+    if (static_cast<int64_t>(n_seqs) * H > int64_t(0x7fffffff) / 16) return KDA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||
+        !aligned16(z) || !aligned16(A) || !aligned16(o) || (initial_state && !aligned16(initial_state)) ||
+        (final_state && !aligned16(final_state)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)))
+        return KDA_ERR_ALIGN;
+    if (initial_state && final_state && initial_state != final_state) {
+        const uintptr_t bytes = static_cast<uintptr_t>(n_seqs) * H * dk * dv * sizeof(float);
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(initial_state);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(final_state);
+        if (a0 < b0 + bytes && b0 < a0 + bytes) return KDA_ERR_SHAPE;  // partial overlap
+    }
+    const size_t need = kda_prefill_workspace_size(total, n_seqs, H, dk, dv, dt);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (total == 0 && !final_state) return KDA_OK;
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.z = z; a.A = A; a.g_min = g_min;
+    a.s0 = initial_state; a.sN = final_state; a.cu = cu_seqlens; a.n_seqs = n_seqs;
+    a.T = cu_seqlens ? 0 : T_or_total; a.H = H; a.o = o; a.npairs = n_seqs * H;
+    // One 128-column slice per workgroup (8 waves) once there are enough (sequence, head)
+    // chains to fill the device; otherwise two 64-column slices (4 waves each).
+    int waves = 4;
+    if (dk == 128 && a.npairs >= compute_units()) waves = 8;
+    return kda::launch_prefill(a, dk, dt == KDA_BF16, waves, stream) == hipSuccess ? KDA_OK
+                                                                                  : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const void* v,
+                           const void* beta, const float* z, const float* A, float g_min,
+                           float* state, int N, int H, int dk, int dv, void* o,
+                           hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (N > 0 && (!q || !k || !v || !beta || !z || !A || !state || !o)) return KDA_ERR_NULL;
+    if (!supported_d(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(g_min) || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(N) * H > int64_t(0x7fffffff)) return KDA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||
+        !aligned16(z) || !aligned16(A) || !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    if (N == 0) return KDA_OK;
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.z = z; a.A = A; a.g_min = g_min;
+    a.state = state; a.N = N; a.H = H; a.o = o;
+    return kda::launch_decode(a, dk, dt == KDA_BF16, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

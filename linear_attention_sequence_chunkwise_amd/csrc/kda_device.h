@@ -1,0 +1,92 @@
+// kda_device.h -- device-side helpers shared by the gfx950 KDA kernels.
+//
+// bf16 values are kept as raw 16-bit patterns (uint16_t) in memory; conversion from fp32
+// uses the hardware round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950).
+// Matrix products use the CDNA4 bf16 MFMA instructions with fp32 accumulation:
+//   mfma32: v_mfma_f32_16x16x32_bf16   A 16x32, B 32x16, 8 bf16 per lane per operand
+//   mfma16: v_mfma_f32_16x16x16_bf16   A 16x16, B 16x16, 4 bf16 per lane per operand
+// Lane layout of a 16x16 fp32 result (wave64, lane l, g = l/16, r = 0..3): row 4g+r,
+// column l%16.  Operand lanes supply row (A) or column (B) l%16; the K positions a lane
+// supplies are indexed by (g, slot) identically for A and B, so any consistent
+// assignment of logical K indices to (g, slot) yields the same contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    __bf16 b = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two fp32 -> two bf16 packed into 32 bits (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 2^x and 1/x on the hardware transcendental unit (about 1 ulp in fp32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4_t v) {
+    return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+// --- element loads of the caller's tensor type -------------------------------------------
+
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16_t> {
+    // 8 consecutive elements -> 8 bf16 (16 bytes)
+    __device__ __forceinline__ static uint4 load8(const bf16_t* p) {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+    __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static void store1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+template <> struct Elem<float> {
+    __device__ __forceinline__ static uint4 load8(const float* p) {
+        float4 a = reinterpret_cast<const float4*>(p)[0];
+        float4 b = reinterpret_cast<const float4*>(p)[1];
+        return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                          pack_bf16x2(b.z, b.w));
+    }
+    __device__ __forceinline__ static float load1(const float* p) { return *p; }
+    __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+// Start token of sequence n: cu_seqlens[n] when given, else n * T (equal-length batch).
+__device__ __forceinline__ int64_t seq_start(const int32_t* cu, int64_t T, int n) {
+    return cu ? static_cast<int64_t>(cu[n]) : static_cast<int64_t>(n) * T;
+}
+
+}  // namespace kda

@@ -1,0 +1,61 @@
+// kda_launch.h -- internal launch interface between the C ABI (kda_api.cpp) and the kernels.
+// Arguments here have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct GateArgs {
+    const float* z;
+    const float* A;
+    float* g;        // nullable
+    float* gcum;     // nullable
+    int64_t total;
+    int H, dk;
+    const int32_t* cu;  // nullable => n_seqs sequences of T tokens
+    int n_seqs;
+    int64_t T;
+    int chunk;
+    float g_min;
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const float* z;
+    const float* A;
+    float g_min;
+    const float* s0;    // nullable
+    float* sN;          // nullable
+    const int32_t* cu;  // nullable => N sequences of T tokens
+    int n_seqs;
+    int64_t T;
+    int H;
+    void* o;
+    int npairs;         // n_seqs * H
+    int nslices;        // set by the launcher
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const float* z;
+    const float* A;
+    float g_min;
+    float* state;
+    int N, H;
+    void* o;
+};
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+// waves: 8 (one dv slice of 128 per workgroup) or 4 (slices of 64); dk = dv in {64, 128}
+hipError_t launch_prefill(const PrefillArgs& a, int dk, bool bf16, int waves, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
+
+}  // namespace kda

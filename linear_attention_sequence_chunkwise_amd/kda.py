@@ -1,0 +1,166 @@
+"""Thin ctypes binding of libkda.so (include/kda.h).  Argument marshalling only: every step
+of the computation runs in the HIP kernels.  PyTorch supplies device memory and the stream.
+
+There is no fallback: if libkda.so is missing or no GPU is present the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK = 0
+KDA_F32 = 0
+KDA_BF16 = 1
+G_MIN = -5.0
+
+# exported symbols, in the order include/kda.h declares them
+SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step",
+           "kda_status_str")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {status_str(code)} ({code})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m linear_attention_sequence_chunkwise_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.kda_status_str.argtypes = [i32]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_gate.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, f32, vp]
+    lib.kda_gate.restype = i32
+    lib.kda_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.kda_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.kda_prefill_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32,
+                                    i32, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_prefill_fwd.restype = i32
+    lib.kda_decode_step.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, vp,
+                                    vp]
+    lib.kda_decode_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load_library().kda_status_str(int(code)).decode()
+
+
+kda_status_str = status_str
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bf16 or fp32)")
+
+
+def _check(fn: str, code: int):
+    if code != KDA_OK:
+        raise KDAError(fn, code)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
+             gcum: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+             n_seqs: int = 1, chunk: int = 64, g_min: float = G_MIN, want_g: bool = True,
+             want_gcum: bool = True, stream=None):
+    """g = g_min*Sigmoid(e^A z) and its chunk-local inclusive cumsum; z [T,H,dk], A [H,dk]."""
+    lib = load_library()
+    T, H, dk = z.shape
+    if g is None and want_g:
+        g = torch.empty_like(z)
+    if gcum is None and want_gcum:
+        gcum = torch.empty_like(z)
+    if cu_seqlens is not None:
+        n_seqs = cu_seqlens.numel() - 1
+    _dev(z, A, g, gcum, cu_seqlens)
+    _check("kda_gate", lib.kda_gate(_ptr(z), _ptr(A), _ptr(g), _ptr(gcum), T, H, dk,
+                                    _ptr(cu_seqlens), n_seqs, chunk, g_min, _stream(stream)))
+    return g, gcum
+
+
+def kda_prefill_workspace_size(total_tokens: int, n_seqs: int, H: int, dk: int, dv: int,
+                               dtype: torch.dtype = torch.bfloat16) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_prefill_workspace_size(total_tokens, n_seqs, H, dk, dv, code))
+
+
+def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=None,
+                    final_state=None, cu_seqlens=None, n_seqs: Optional[int] = None, o=None,
+                    workspace=None, stream=None):
+    """Chunkwise prefill over packed tokens.  q,k,z [total,H,dk]; v [total,H,dv];
+    beta [total,H]; A [H,dk]; states [N,H,dk,dv] fp32; cu_seqlens [N+1] int32 or None (then
+    n_seqs equal-length sequences, default 1).  Returns o [total,H,dv]."""
+    lib = load_library()
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        T_or_total = total
+    else:
+        N = 1 if n_seqs is None else int(n_seqs)
+        if total % N:
+            raise ValueError("total tokens not divisible by n_seqs")
+        T_or_total = total // N
+    if o is None:
+        o = torch.empty((total, H, dv), dtype=q.dtype, device=q.device)
+    need = kda_prefill_workspace_size(total, N, H, dk, dv, q.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _dev(q, k, v, beta, z, A, initial_state, final_state, cu_seqlens, o, workspace)
+    _check("kda_prefill_fwd", lib.kda_prefill_fwd(
+        dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(initial_state),
+        _ptr(final_state), _ptr(cu_seqlens), N, T_or_total, H, dk, dv, _ptr(o), _ptr(workspace),
+        wbytes, _stream(stream)))
+    return o
+
+
+def kda_decode_step(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, stream=None):
+    """One decode step; q,k,z [N,H,dk]; v [N,H,dv]; beta [N,H]; state [N,H,dk,dv] fp32 is
+    updated in place.  Returns o [N,H,dv]."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, beta, z, A, state, o)
+    _check("kda_decode_step", lib.kda_decode_step(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
+        _ptr(state), N, H, dk, dv, _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,119 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol include/kda.h declares,
+and rejects invalid arguments on the host before anything is launched (no GPU needed: every
+call below fails validation, so no HIP call is made)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_sequence_chunkwise_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x10004)  # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(kda.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_status_strings(lib):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP):
+        s = kda.status_str(code)
+        assert s.startswith("KDA_"), s
+    assert "unknown" in kda.status_str(42)
+
+
+def prefill(lib, dt=BF16, q=P, k=P, v=P, beta=P, z=P, A=P, g_min=-5.0, s0=None, sN=None,
+            cu=None, N=1, T=64, H=2, dk=128, dv=128, o=P, ws=None, wsb=0):
+    return lib.kda_prefill_fwd(dt, q, k, v, beta, z, A, g_min, s0, sN, cu, N, T, H, dk, dv, o,
+                               ws, wsb, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert prefill(lib, dt=7) == EUNSUP
+    assert prefill(lib, A=None) == ENULL
+    assert prefill(lib, T=0, q=None, k=None, v=None, beta=None, z=None, o=None) == OK
+    for name in ("q", "k", "v", "beta", "z", "A", "o"):
+        assert prefill(lib, **{name: None}) == ENULL, name
+    assert prefill(lib, N=0) == ESHAPE
+    assert prefill(lib, T=-1) == ESHAPE
+    assert prefill(lib, H=0) == ESHAPE
+    assert prefill(lib, dk=96, dv=96) == EUNSUP
+    assert prefill(lib, dk=128, dv=64) == EUNSUP
+    assert prefill(lib, g_min=-5.5) == EUNSUP      # outside the 16-token tile bound
+    assert prefill(lib, g_min=0.0) == EUNSUP
+    assert prefill(lib, g_min=float("nan")) == EUNSUP
+    assert prefill(lib, q=MIS) == EALIGN
+    assert prefill(lib, s0=MIS) == EALIGN
+    assert prefill(lib, cu=ctypes.c_void_p(0x10002)) == EALIGN
+    # a final state that partially overlaps the initial state
+    assert prefill(lib, s0=ctypes.c_void_p(0x100000), sN=ctypes.c_void_p(0x100010)) == ESHAPE
+    assert prefill(lib, T=1 << 45, N=1 << 10) == ESHAPE
+
+
+def test_gate_rejects_bad_arguments(lib):
+    def gate(z=P, A=P, g=P, gc=P, T=64, H=2, dk=128, cu=None, N=1, chunk=64, g_min=-5.0):
+        return lib.kda_gate(z, A, g, gc, T, H, dk, cu, N, chunk, g_min, None)
+    assert gate(z=None) == ENULL
+    assert gate(g=None, gc=None) == ENULL
+    assert gate(T=-1) == ESHAPE
+    assert gate(dk=6) == EUNSUP
+    assert gate(chunk=0) == ESHAPE
+    assert gate(chunk=4096) == ESHAPE
+    assert gate(g_min=1.0) == EUNSUP
+    assert gate(T=65, N=2) == ESHAPE
+    assert gate(z=MIS) == EALIGN
+    assert gate(T=0) == OK  # nothing to do, nothing launched
+    assert gate(T=0, z=None, g=None, gc=None) == OK  # no tokens: per-token pointers unused
+    assert gate(A=None) == ENULL
+
+
+def test_decode_rejects_bad_arguments(lib):
+    def dec(dt=BF16, q=P, state=P, N=4, H=2, dk=128, dv=128, g_min=-5.0, o=P):
+        return lib.kda_decode_step(dt, q, P, P, P, P, P, g_min, state, N, H, dk, dv, o, None)
+    assert dec(q=None) == ENULL
+    assert dec(state=None) == ENULL
+    assert dec(N=-1) == ESHAPE
+    assert dec(dk=32, dv=32) == EUNSUP
+    assert dec(state=MIS) == EALIGN
+    assert dec(dt=3) == EUNSUP
+    assert dec(N=0) == OK
+    assert dec(N=0, q=None, state=None, o=None) == OK
+
+
+def test_workspace_size_is_aligned(lib):
+    for args in [(4096, 1, 16, 128, 128, BF16), (293000, 64, 32, 128, 128, BF16), (256, 1, 2, 64, 64, F32)]:
+        assert lib.kda_prefill_workspace_size(*args) % 256 == 0
+
+
+def test_binding_fails_loudly_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    z = torch.zeros(4, 1, 4)
+    with pytest.raises(Exception):
+        kda.kda_gate(z, torch.zeros(1, 4))
