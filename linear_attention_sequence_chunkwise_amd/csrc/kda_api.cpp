@@ -102,6 +102,8 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     if (!cu_seqlens && n_seqs > 0 && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
     if (total > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
     if (static_cast<int64_t>(n_seqs) * H > int64_t(0x7fffffff) / 16) return KDA_ERR_SHAPE;
+    // 64 token rows of one chunk must span < 2^31 bytes (32-bit buffer offsets)
+    if (static_cast<int64_t>(H) * dk * 4 * 64 >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||
         !aligned16(z) || !aligned16(A) || !aligned16(o) || (initial_state && !aligned16(initial_state)) ||
         (final_state && !aligned16(final_state)) ||

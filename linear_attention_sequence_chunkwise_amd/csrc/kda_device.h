@@ -60,6 +60,40 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4_t v) {
     return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
+// --- buffer (SGPR-descriptor) memory access ----------------------------------------------
+// A raw buffer covers [base, base + nbytes).  Loads at byte offsets >= nbytes return zero
+// and stores there are dropped, so a descriptor rebased at a chunk's first token with
+// nbytes = (valid rows) x (row bytes) masks the rows past a sequence's end without any
+// per-lane test, and addressing needs no 64-bit per-lane arithmetic.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(nbytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
 // --- element loads of the caller's tensor type -------------------------------------------
 
 template <typename T> struct Elem;
@@ -83,6 +117,16 @@ template <> struct Elem<float> {
     __device__ __forceinline__ static float load1(const float* p) { return *p; }
     __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
 };
+
+// Workgroup barrier that orders LDS accesses only.  A full __syncthreads() also waits for
+// every outstanding global load and store of the thread (s_waitcnt vmcnt(0)), which would
+// stall on in-flight prefetches and output stores; LDS is the only memory the workgroup's
+// threads exchange through.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Start token of sequence n: cu_seqlens[n] when given, else n * T (equal-length batch).
 __device__ __forceinline__ int64_t seq_start(const int32_t* cu, int64_t T, int n) {
