@@ -156,10 +156,13 @@ def main():
     sN = torch.empty((inp.N, inp.H, inp.dk, inp.dv), dtype=torch.float32, device="cuda") \
         if want_final else None
     o = torch.empty((inp.total, inp.H, inp.dv), dtype=q.dtype, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_size(inp.total, inp.N, inp.H, inp.dk, inp.dv, q.dtype),
+                     dtype=torch.uint8, device="cuda")
 
     def step():
         kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=sN,
-                            cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o)
+                            cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o,
+                            workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -196,6 +199,7 @@ def main():
         "config": {"workload": name, "sequences": inp.N, "total_tokens": inp.total,
                    "heads": inp.H, "dk": inp.dk, "dv": inp.dv, "chunk": CHUNK,
                    "initial_state": s0 is not None, "final_state": sN is not None,
+                   "workspace_bytes": int(ws.numel()),
                    "cache": "warm: back-to-back calls"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,

@@ -86,8 +86,11 @@ kda_status kda_gate(const float* z, const float* A, float* g, float* gcum,
 
 /*
  * kda_prefill_workspace_size -- bytes of device workspace kda_prefill_fwd needs for this
- * problem (a multiple of 256; may be 0).  Returns 0 for invalid sizes as well; the
- * prefill call reports those.
+ * problem (a multiple of 256).  The prefill runs in two kernels: the first computes every
+ * (chunk, head)'s intra-chunk factors in parallel into the workspace (58.5 KiB per chunk and
+ * head at d = 128, 34 KiB at d = 64, for at most ceil(total/64) + n_seqs chunks); the
+ * second runs the serial inter-chunk state pass over them.  The workspace also holds the
+ * varlen chunk table.  Returns 0 for invalid sizes; the prefill call reports those.
  */
 size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
                                   kda_dtype dt);
@@ -113,8 +116,9 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int d
  *   T_or_total     tokens per sequence when cu_seqlens is NULL, else the packed total
  *   dk, dv         64 or 128 each, dk == dv
  *   o              [total, H, dv] output of type dt
- *   workspace      device scratch of at least kda_prefill_workspace_size(...) bytes
- *                  (may be NULL when that size is 0); contents on return are undefined
+ *   workspace      device scratch of at least kda_prefill_workspace_size(...) bytes,
+ *                  16-byte aligned (KDA_ERR_WORKSPACE otherwise); may be NULL only when
+ *                  there is nothing to compute; contents on return are undefined
  * A zero-length sequence writes no output rows and copies its initial state (or zeros) to
  * final_state.  Results equal the token recurrence up to floating-point association.
  */

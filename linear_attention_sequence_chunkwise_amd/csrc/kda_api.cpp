@@ -82,8 +82,10 @@ kda_status kda_gate(const float* z, const float* A, float* g, float* gcum, int64
 
 size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
                                   kda_dtype dt) {
-    (void)total_tokens; (void)n_seqs; (void)H; (void)dk; (void)dv; (void)dt;
-    return 0;  // the fused chain kernel keeps every intermediate on chip
+    (void)dt;
+    if (total_tokens < 0 || n_seqs <= 0 || H <= 0 || !supported_d(dk, dv)) return 0;
+    if (total_tokens > kMaxElems / (static_cast<int64_t>(H) * dk)) return 0;
+    return kda::split_workspace_bytes(total_tokens, n_seqs, H, dk);
 }
 
 kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const void* v,
@@ -101,7 +103,7 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     if (!std::isfinite(g_min) || g_min < -5.f || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
     if (!cu_seqlens && n_seqs > 0 && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
     if (total > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
-    if (static_cast<int64_t>(n_seqs) * H > int64_t(0x7fffffff) / 16) return KDA_ERR_SHAPE;
+    if (static_cast<int64_t>(n_seqs) * H > int64_t(0x7fffffff) / 16 || H > 65535) return KDA_ERR_SHAPE;
     // 64 token rows of one chunk must span < 2^31 bytes (32-bit buffer offsets)
     if (static_cast<int64_t>(H) * dk * 4 * 64 >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||
@@ -115,20 +117,25 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(final_state);
         if (a0 < b0 + bytes && b0 < a0 + bytes) return KDA_ERR_SHAPE;  // partial overlap
     }
+    if (total == 0 && !final_state) return KDA_OK;  // nothing to compute or write
     const size_t need = kda_prefill_workspace_size(total, n_seqs, H, dk, dv, dt);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
-    if (total == 0 && !final_state) return KDA_OK;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
 
-    kda::PrefillArgs a{};
+    kda::SplitArgs a{};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.z = z; a.A = A; a.g_min = g_min;
     a.s0 = initial_state; a.sN = final_state; a.cu = cu_seqlens; a.n_seqs = n_seqs;
     a.T = cu_seqlens ? 0 : T_or_total; a.H = H; a.o = o; a.npairs = n_seqs * H;
-    // One 128-column slice per workgroup (8 waves) once there are enough (sequence, head)
-    // chains to fill the device; otherwise two 64-column slices (4 waves each).
+    a.total = total;
+    const size_t table = ((static_cast<size_t>(n_seqs) + 1) * 4 + 255) / 256 * 256;
+    a.chunk_start = static_cast<int32_t*>(workspace);
+    a.blocks = static_cast<char*>(workspace) + table;
+    // state pass: enough (sequence, head, dv slice) chains to cover the compute units
+    const int cus = compute_units();
     int waves = 4;
-    if (dk == 128 && a.npairs >= compute_units()) waves = 8;
-    return kda::launch_prefill(a, dk, dt == KDA_BF16, waves, stream) == hipSuccess ? KDA_OK
-                                                                                  : KDA_ERR_HIP;
+    if (dk == 128) waves = a.npairs >= cus ? 8 : (2 * a.npairs >= cus ? 4 : 2);
+    else waves = a.npairs >= cus ? 4 : 2;
+    return kda::launch_prefill_split(a, dk, dt == KDA_BF16, waves, stream) == hipSuccess ? KDA_OK
+                                                                                         : KDA_ERR_HIP;
 }
 
 kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const void* v,

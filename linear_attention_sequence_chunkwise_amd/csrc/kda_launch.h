@@ -40,6 +40,20 @@ struct PrefillArgs {
     int nslices;        // set by the launcher
 };
 
+// Two-kernel prefill (intra-chunk factors, then the serial state pass) over a workspace
+// holding the varlen chunk table and one factor block per (chunk, head).
+struct SplitArgs : PrefillArgs {
+    int64_t total;           // packed token count
+    int32_t* chunk_start;    // [n_seqs + 1] in the workspace (varlen only)
+    void* blocks;            // factor blocks in the workspace
+};
+
+size_t split_block_bytes(int dk);
+int64_t split_max_chunks(int64_t total, int n_seqs);
+size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk);
+// state-pass waves: 8 (one dv slice of 128), 4 (slices of 64) or 2 (slices of 32)
+hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int waves, hipStream_t stream);
+
 struct DecodeArgs {
     const void* q;
     const void* k;
