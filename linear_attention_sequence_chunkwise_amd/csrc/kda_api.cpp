@@ -131,10 +131,10 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     a.blocks = static_cast<char*>(workspace) + table;
     // state pass: enough (sequence, head, dv slice) chains to cover the compute units
     const int cus = compute_units();
-    int waves = 4;
-    if (dk == 128) waves = a.npairs >= cus ? 8 : (2 * a.npairs >= cus ? 4 : 2);
-    else waves = a.npairs >= cus ? 4 : 2;
-    return kda::launch_prefill_split(a, dk, dt == KDA_BF16, waves, stream) == hipSuccess ? KDA_OK
+    // d = 128: two workgroups per (sequence, head) (dv slices of 64) while that still fits
+    // the compute units, else one workgroup covering all 128 columns.
+    const int ct = (dk == 128 && 2 * static_cast<int64_t>(a.npairs) > cus) ? 2 : 1;
+    return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ct, stream) == hipSuccess ? KDA_OK
                                                                                          : KDA_ERR_HIP;
 }
 

@@ -94,6 +94,14 @@ __device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// LDS-DMA: the 64 lanes' 16-byte pieces at byte offsets voff of r are written, in lane
+// order, to the contiguous 1 KiB at lds (a workgroup-uniform LDS address), without passing
+// through registers.  Out-of-range lanes write zeros.  Completion is tracked by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
 // --- element loads of the caller's tensor type -------------------------------------------
 
 template <typename T> struct Elem;

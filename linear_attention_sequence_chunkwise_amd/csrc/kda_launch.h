@@ -51,8 +51,8 @@ struct SplitArgs : PrefillArgs {
 size_t split_block_bytes(int dk);
 int64_t split_max_chunks(int64_t total, int n_seqs);
 size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk);
-// state-pass waves: 8 (one dv slice of 128), 4 (slices of 64) or 2 (slices of 32)
-hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int waves, hipStream_t stream);
+// ct: 16-column state tiles per compute wave; a state-pass workgroup covers 64 ct dv columns
+hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ct, hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;
@@ -68,8 +68,6 @@ struct DecodeArgs {
 };
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
-// waves: 8 (one dv slice of 128 per workgroup) or 4 (slices of 64); dk = dv in {64, 128}
-hipError_t launch_prefill(const PrefillArgs& a, int dk, bool bf16, int waves, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
 
 }  // namespace kda

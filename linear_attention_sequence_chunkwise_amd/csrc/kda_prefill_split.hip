@@ -29,7 +29,8 @@
 // products of alpha = e^g, never exponentials of large sums.
 //
 // Factor block of one (chunk, head), bf16 unless noted (offsets in the kernels below):
-//   Kt [64][DK] = K~, Qt [64][DK] = Q~, KnT [DK][64] = (K e^{Gamma_n - Gamma})^T,
+//   Kt = K~ and Qt = Q~ [64 x DK], KnT = (K e^{Gamma_n - Gamma})^T [DK x 64], each stored as
+//   the lane-order image (lane_off, kn_off) that the state pass copies verbatim into LDS,
 //   T and M as their 10 lower 16x16 blocks (row-major, block order (a,b) = a(a+1)/2 + b),
 //   decayN [DK] fp32 = e^{Gamma_n}.
 #include "kda_device.h"
@@ -54,6 +55,25 @@ struct Block {
 };
 
 __device__ __forceinline__ int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
+
+// Byte offset of element (row r, channel ch) of K~ or Q~ inside its lane-order image: piece
+// (a, s) = (r / 16, ch / 32) holds, for lane (g, li), the eight channels 32s + 8g .. of row
+// 16a + li -- exactly the 16 bytes that lane feeds to a 16x16x32 MFMA.
+template <int DK>
+__device__ __forceinline__ uint32_t lane_off(int r, int ch) {
+    return static_cast<uint32_t>((((r >> 4) * (DK / 32) + (ch >> 5)) * 64 + ((ch >> 3) & 3) * 16 + (r & 15)) * 16 +
+                                 (ch & 7) * 2);
+}
+
+// Byte offset of the four tokens t4 .. t4 + 3 (t4 a multiple of 4) of channel c in the
+// lane-order image of K^n^T.  The state-update product uses state row tile m with rows
+// pi(m, i) = 32 (m / 2) + 8 (i / 4) + 4 (m % 2) + i % 4; piece (m, sp) holds for lane (g, li)
+// the tokens 32sp + 4g .. and 32sp + 16 + 4g .. of channel pi(m, li).
+__device__ __forceinline__ uint32_t kn_off(int c, int t4) {
+    const int m = 2 * (c >> 5) + ((c >> 2) & 1), li = 4 * ((c >> 3) & 3) + (c & 3);
+    const int u = t4 & 31;
+    return static_cast<uint32_t>(((m * 2 + (t4 >> 5)) * 64 + ((u & 15) >> 2) * 16 + li) * 16 + (u >> 4) * 8);
+}
 
 // Column-operand scale index of tile pair (a, b): -1 means 1.
 __device__ __forceinline__ int colscale_index(int a, int b) {
@@ -304,16 +324,16 @@ __global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
             *reinterpret_cast<uint32_t*>(&sm.u.ops.Kr[r][ch0]) = pack_bf16x2(kf.x * F.x, kf.y * F.y);
             *reinterpret_cast<uint32_t*>(&sm.u.ops.Qr[r][ch0]) = pack_bf16x2(qf.x * F.x, qf.y * F.y);
             *reinterpret_cast<uint32_t*>(&sm.u.ops.Kc[r][ch0]) = pack_bf16x2(kf.x * E[i].x, kf.y * E[i].y);
-            *reinterpret_cast<uint32_t*>(blk + B::KT + (r * DK + ch0) * 2) = pack_bf16x2(kf.x * FR.x, kf.y * FR.y);
-            *reinterpret_cast<uint32_t*>(blk + B::QT + (r * DK + ch0) * 2) = pack_bf16x2(qf.x * FR.x, qf.y * FR.y);
+            *reinterpret_cast<uint32_t*>(blk + B::KT + lane_off<DK>(r, ch0)) = pack_bf16x2(kf.x * FR.x, kf.y * FR.y);
+            *reinterpret_cast<uint32_t*>(blk + B::QT + lane_off<DK>(r, ch0)) = pack_bf16x2(qf.x * FR.x, qf.y * FR.y);
             kn[i] = make_float2(kf.x * (E[i].x * eN.x), kf.y * (E[i].y * eN.y));
         }
 #pragma unroll
         for (int j = 0; j < SEG / 4; ++j) {
             const int tk = iseg * SEG + 4 * j;
-            *reinterpret_cast<uint2*>(blk + B::KN + (ch0 * kC + tk) * 2) =
+            *reinterpret_cast<uint2*>(blk + B::KN + kn_off(ch0, tk)) =
                 make_uint2(pack_bf16x2(kn[4 * j].x, kn[4 * j + 1].x), pack_bf16x2(kn[4 * j + 2].x, kn[4 * j + 3].x));
-            *reinterpret_cast<uint2*>(blk + B::KN + ((ch0 + 1) * kC + tk) * 2) =
+            *reinterpret_cast<uint2*>(blk + B::KN + kn_off(ch0 + 1, tk)) =
                 make_uint2(pack_bf16x2(kn[4 * j].y, kn[4 * j + 1].y), pack_bf16x2(kn[4 * j + 2].y, kn[4 * j + 3].y));
         }
         if (iseg == 0) {
@@ -455,45 +475,47 @@ __global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
     }
 }
 
-// ---- K2: serial state pass ----------------------------------------------------------------
-template <int DK, int NW>
-struct StateSmem {
-    static constexpr int NT = 64 * NW;
-    static constexpr int DVS = 16 * NW;
-    static constexpr int KROW = DK + 16;
-    static constexpr int TROW = kC + 8;
-    static constexpr int VROW = DVS + 16;
-    bf16_t Kt[kC][KROW];
-    bf16_t Qt[kC][KROW];
-    bf16_t KnT[DK][TROW];
-    bf16_t T[kC][TROW];    // lower 16x16 blocks used
-    bf16_t M[kC][TROW];
-    bf16_t V[kC][VROW];    // v of this slice; each wave's 16 columns then stage its O
+// ---- K2: serial state pass -----------------------------------------------------------------
+// Eight waves per workgroup: waves 0-3 compute, waves 4-7 copy the next chunk's factor block
+// and v slice from global memory straight into the other half of a double-buffered LDS stage
+// with LDS-DMA loads (buffer_load_dwordx4 ... lds: each instruction writes one contiguous
+// 1 KiB piece, 16 bytes per lane, without passing through registers), while the compute waves
+// work on the current half.  One workgroup barrier per chunk.  The factor block is stored by
+// the intra-chunk kernel in exactly this LDS layout, with the operands of the big products in
+// lane order, so every compute read of them is a linear, conflict-free ds_read_b128.
+//
+// Compute wave cw owns dv columns [col0, col0 + 16 CT) of the state, in registers:
+//   Sacc[ct][m][r] = S[pi(m, 4g + r)][col0 + 16 ct + li],
+// so that bf16-packing Sacc[ct][2s], Sacc[ct][2s+1] gives, per lane, the eight channels
+// 32 s + 8 g + e, which is both the B operand of X = K~ S and the A operand of Y^T = S^T Q~^T.
+// O is produced transposed (O^T = Y^T + R^T M^T), which leaves each lane with four adjacent
+// output columns of one token: one 8-byte store per tile, no staging.
+template <int DK, int DVS, typename TIn>
+struct StateBuf {
+    static constexpr int NBP = static_cast<int>((Block<DK>::BYTES + 1023) / 1024);  // block pieces
+    static constexpr int VRB = DVS * static_cast<int>(sizeof(TIn));                 // v row bytes
+    static constexpr int VRP = 1024 / VRB;                                          // v rows per piece
+    static constexpr int NVP = kC / VRP;                                            // v pieces
+    static constexpr int VPS = 1024 + 32;  // padded piece stride: rows 4 apart fall in other banks
+    uint4 blk[NBP * 64];                   // the factor block (the last piece may run past it)
+    unsigned char v[NVP * VPS];            // v slice, rows of VRB bytes, VRP rows per piece
     float beta[kC];
-    float decayN[DK];
 };
 
-template <int DK, int NW, typename TIn>
-__global__ void __launch_bounds__(NW * 64, 1) prefill_state_kernel(SplitArgs args) {
-    using Smem = StateSmem<DK, NW>;
+template <int DK, int CT, typename TIn>
+__global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
+    constexpr int DVS = 64 * CT;  // columns per workgroup (4 compute waves x 16 CT)
+    using Buf = StateBuf<DK, DVS, TIn>;
     using P = Pair<TIn>;
     using B = Block<DK>;
-    constexpr int NT = Smem::NT;
-    constexpr int DVS = Smem::DVS;
-    constexpr int KSTEPS = DK / 32;
+    constexpr int KS = DK / 32;
     constexpr int MT = DK / 16;
     constexpr int ES = static_cast<int>(sizeof(TIn));
-    // 16-byte pieces of one factor block and of the v slice
-    constexpr int NKT = kC * DK / 8;             // per Kt / Qt / KnT
-    constexpr int NTB = 10 * 32;                 // per T / M
-    constexpr int NDN = DK / 4;
-    constexpr int NV = kC * DVS / 8;
-    constexpr int PK = NKT / NT;                 // Kt, Qt, KnT pieces per thread
-    constexpr int PT = (NTB + NT - 1) / NT;      // T, M pieces per thread (guarded)
-    constexpr int PV = NV / NT;
-    static_assert(NKT % NT == 0 && NV % NT == 0 && PV >= 1, "piece split");
+    constexpr int NBP = Buf::NBP, NVP = Buf::NVP, VRP = Buf::VRP, VRB = Buf::VRB;
+    constexpr int LPR = VRB / 16;  // lanes per v row
+    static_assert(VRP * VRB == 1024 && NVP * VRP == kC, "v pieces");
 
-    __shared__ Smem sm;
+    __shared__ Buf sm[2];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -516,184 +538,187 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_state_kernel(SplitArgs arg
         len = args.T;
         slot0 = n * static_cast<int>((args.T + kC - 1) / kC);
     }
+    const int nchunks = static_cast<int>((len + kC - 1) / kC);
     const int dv = DK;
-    const int col0 = slice * DVS + 16 * w;
     const uint32_t rowV = static_cast<uint32_t>(H) * dv * ES;
-    const uint32_t rowB = static_cast<uint32_t>(H) * ES;
-    const char* vbase = static_cast<const char*>(args.v) + (static_cast<size_t>(h) * dv + slice * DVS) * ES;
-    const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
-    char* obase = static_cast<char*>(args.o) + (static_cast<size_t>(h) * dv + col0) * ES;
-    const char* blocks = static_cast<const char*>(args.blocks);
 
-    f32x4_t Sacc[MT];  // Sacc[m][r] = S[pi(m, 4g + r)][col0 + li]
+    if (w >= 4) {
+        // ================================ loader waves ================================
+        const int lw = w - 4;
+        const uint32_t rowB = static_cast<uint32_t>(H) * ES;
+        const char* vbase = static_cast<const char*>(args.v) + (static_cast<size_t>(h) * dv + slice * DVS) * ES;
+        const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
+        const char* blocks = static_cast<const char*>(args.blocks);
+        // issue the copies of chunk c into stage b; wave 4 also fetches beta into a register
+        auto issue = [&](int c, Buf& b, float& rb) __attribute__((always_inline)) {
+            const int64_t rem = len - static_cast<int64_t>(c) * kC;
+            const int clen = rem < kC ? static_cast<int>(rem) : kC;
+            const int64_t t0 = tok0 + static_cast<int64_t>(c) * kC;
+            const rsrc_t rf = make_rsrc(blocks + (static_cast<size_t>(slot0 + c) * H + h) * B::BYTES, B::BYTES);
+            for (int p = lw; p < NBP; p += 4)
+                dma16(rf, &b.blk[p * 64], p * 1024 + lane * 16);
+            const rsrc_t rvs = make_rsrc(vbase + t0 * rowV, clen * rowV);
+            for (int j = lw; j < NVP; j += 4)
+                dma16(rvs, &b.v[j * Buf::VPS], (j * VRP + lane / LPR) * rowV + (lane % LPR) * 16);
+            if (lw == 0) {
+                const rsrc_t rbs = make_rsrc(bbase + t0 * rowB, clen * rowB);
+                rb = P::load_beta(rbs, lane * rowB);
+            }
+        };
+        float rb = 0.f;
+        if (nchunks > 0) {
+            issue(0, sm[0], rb);
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lw == 0) sm[0].beta[lane] = rb;
+        }
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                Buf& b = sm[(c + 1) & 1];
+                issue(c + 1, b, rb);
+                __builtin_amdgcn_s_waitcnt(0);
+                if (lw == 0) b.beta[lane] = rb;
+            }
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ================================ compute waves ================================
+    const int col0 = slice * DVS + 16 * CT * w;
+    char* obase = static_cast<char*>(args.o) + (static_cast<size_t>(h) * dv + col0) * ES;
+
+    f32x4_t Sacc[CT][MT];
     const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * dv + col0 + li;
     if (args.s0) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sacc[m][r] = args.s0[sbase + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv];
-    } else {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) Sacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // prefetch registers for one chunk
-    uint4 pkt[PK], pqt[PK], pkn[PK], ptb[PT], pmb[PT];
-    uint4 pdn = make_uint4(0, 0, 0, 0);
-    typename P::Row8 pv[PV];
-    float pb = 0.f;
-    auto issue_loads = [&](int64_t t0, int clen, int slot) __attribute__((always_inline)) {
-        const rsrc_t rf = make_rsrc(blocks + (static_cast<size_t>(slot) * H + h) * B::BYTES, B::BYTES);
-#pragma unroll
-        for (int i = 0; i < PK; ++i) {
-            const uint32_t p = static_cast<uint32_t>(tid + i * NT) * 16;
-            pkt[i] = bload16(rf, B::KT + p);
-            pqt[i] = bload16(rf, B::QT + p);
-            pkn[i] = bload16(rf, B::KN + p);
-        }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const uint32_t p = static_cast<uint32_t>(tid + i * NT);
-            ptb[i] = p < NTB ? bload16(rf, B::TB + p * 16) : make_uint4(0, 0, 0, 0);
-            pmb[i] = p < NTB ? bload16(rf, B::MB + p * 16) : make_uint4(0, 0, 0, 0);
-        }
-        if (tid < NDN) pdn = bload16(rf, B::DN + tid * 16);
-        const rsrc_t rv = make_rsrc(vbase + t0 * rowV, clen * rowV);
-#pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int idx = tid + i * NT, r = idx / (DVS / 8), o8 = (idx % (DVS / 8)) * 8;
-            pv[i] = P::load8(rv, r * rowV + o8 * ES);
-        }
-        const rsrc_t rb = make_rsrc(bbase + t0 * rowB, clen * rowB);
-        pb = P::load_beta(rb, (tid & (kC - 1)) * rowB);
-    };
-    if (len > 0) issue_loads(tok0, len < kC ? static_cast<int>(len) : kC, slot0);
-
-    int slot = slot0;
-    for (int64_t c0 = 0; c0 < len; c0 += kC, ++slot) {
-        const int clen = static_cast<int>(len - c0 < kC ? len - c0 : kC);
-        const int64_t t0 = tok0 + c0;
-
-        lds_barrier();  // the previous chunk's readers are done
-        // ---- copy the prefetched chunk into LDS ---------------------------------------
-#pragma unroll
-        for (int i = 0; i < PK; ++i) {
-            const int p = tid + i * NT;
-            const int r = p / (DK / 8), c8 = (p % (DK / 8)) * 8;  // Kt/Qt: row r, channel c8
-            *reinterpret_cast<uint4*>(&sm.Kt[r][c8]) = pkt[i];
-            *reinterpret_cast<uint4*>(&sm.Qt[r][c8]) = pqt[i];
-            const int rn = p / (kC / 8), t8 = (p % (kC / 8)) * 8;  // KnT: row channel, token t8
-            *reinterpret_cast<uint4*>(&sm.KnT[rn][t8]) = pkn[i];
-        }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int p = tid + i * NT;
-            if (p < NTB) {
-                const int bi = p / 32, piece = p % 32, row = piece >> 1, half = piece & 1;
-                const int a = bi < 1 ? 0 : bi < 3 ? 1 : bi < 6 ? 2 : 3;
-                const int b = bi - (a * (a + 1)) / 2;
-                *reinterpret_cast<uint4*>(&sm.T[16 * a + row][16 * b + 8 * half]) = ptb[i];
-                *reinterpret_cast<uint4*>(&sm.M[16 * a + row][16 * b + 8 * half]) = pmb[i];
-            }
-        }
-        if (tid < NDN) *reinterpret_cast<uint4*>(&sm.decayN[4 * tid]) = pdn;
-#pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int idx = tid + i * NT, r = idx / (DVS / 8), o8 = (idx % (DVS / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.V[r][o8]) = P::bf16x8(pv[i]);
-        }
-        if (tid < kC) sm.beta[tid] = pb;
-        if (c0 + kC < len) {
-            const int64_t rem = len - c0 - kC;
-            issue_loads(t0 + kC, rem < kC ? static_cast<int>(rem) : kC, slot + 1);
-        }
-        lds_barrier();
-
-        // ---- X = K~ S, Y = Q~ S, R = beta (V - X) (wave-local from here on) --------------
-        uint4 Sb[KSTEPS];  // bf16 S as B operand: slot e of lane g <-> channel 32s+8g+e
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            Sb[s] = make_uint4(pack_bf16x2(Sacc[2 * s][0], Sacc[2 * s][1]),
-                               pack_bf16x2(Sacc[2 * s][2], Sacc[2 * s][3]),
-                               pack_bf16x2(Sacc[2 * s + 1][0], Sacc[2 * s + 1][1]),
-                               pack_bf16x2(Sacc[2 * s + 1][2], Sacc[2 * s + 1][3]));
-        f32x4_t Y[4];
-        uint2 Rb[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4_t X = {0.f, 0.f, 0.f, 0.f};
-            Y[a] = X;
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const int ch = 32 * s + 8 * g;
-                X = mfma32(*reinterpret_cast<const uint4*>(&sm.Kt[16 * a + li][ch]), Sb[s], X);
-                Y[a] = mfma32(*reinterpret_cast<const uint4*>(&sm.Qt[16 * a + li][ch]), Sb[s], Y[a]);
-            }
-            const float4 bb = *reinterpret_cast<const float4*>(&sm.beta[16 * a + 4 * g]);
-            const int vc = 16 * w + li;
-            f32x4_t R;
-            R[0] = bb.x * (bf16_to_f32(sm.V[16 * a + 4 * g + 0][vc]) - X[0]);
-            R[1] = bb.y * (bf16_to_f32(sm.V[16 * a + 4 * g + 1][vc]) - X[1]);
-            R[2] = bb.z * (bf16_to_f32(sm.V[16 * a + 4 * g + 2][vc]) - X[2]);
-            R[3] = bb.w * (bf16_to_f32(sm.V[16 * a + 4 * g + 3][vc]) - X[3]);
-            Rb[a] = pack_bf16x4(R);  // B operand: k = token 4g + r of tile a
-        }
-        // ---- U = T R, O = Y + M R ---------------------------------------------------------
-        uint2 Ub[4];
-        const rsrc_t ro = make_rsrc(obase + t0 * rowV, clen * rowV);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-            f32x4_t O = Y[a];
-#pragma unroll
-            for (int b = 0; b <= a; ++b) {
-                U = mfma16(*reinterpret_cast<const uint2*>(&sm.T[16 * a + li][16 * b + 4 * g]), Rb[b], U);
-                O = mfma16(*reinterpret_cast<const uint2*>(&sm.M[16 * a + li][16 * b + 4 * g]), Rb[b], O);
-            }
-            Ub[a] = pack_bf16x4(U);
-            if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm.V[16 * a + 4 * g + r][16 * w + li] = f32_to_bf16(O[r]);
-            } else {
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    bstore4(ro, (16 * a + 4 * g + r) * rowV + li * 4, __float_as_uint(O[r]));
+                    Sacc[ct][m][r] = args.s0[sbase + 16 * ct +
+                                             static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv];
+    } else {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) Sacc[ct][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    lds_barrier();
+
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nchunks; ++c) {
+        const Buf& b = sm[c & 1];
+        const uint4* kt = b.blk + B::KT / 16;
+        const uint4* qt = b.blk + B::QT / 16;
+        const uint4* kn = b.blk + B::KN / 16;
+        const uint2* tb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
+        const uint2* mb = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
+        const float* dnv = reinterpret_cast<const float*>(b.blk + B::DN / 16);
+        const int64_t rem = len - static_cast<int64_t>(c) * kC;
+        const int clen = rem < kC ? static_cast<int>(rem) : kC;
+        const int64_t t0 = tok0 + static_cast<int64_t>(c) * kC;
+        const rsrc_t ro = make_rsrc(obase + t0 * rowV, clen * rowV);
+
+        uint4 Sb[CT][KS];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                Sb[ct][s] = make_uint4(pack_bf16x2(Sacc[ct][2 * s][0], Sacc[ct][2 * s][1]),
+                                       pack_bf16x2(Sacc[ct][2 * s][2], Sacc[ct][2 * s][3]),
+                                       pack_bf16x2(Sacc[ct][2 * s + 1][0], Sacc[ct][2 * s + 1][1]),
+                                       pack_bf16x2(Sacc[ct][2 * s + 1][2], Sacc[ct][2 * s + 1][3]));
+        uint2 Rb[4][CT], Ub[4][CT];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            // X = K~ S (rows: tokens 4g + r of tile a), Y^T = S^T Q~^T (rows: columns 4g + r)
+            f32x4_t X[CT], Yt[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) { X[ct] = zero; Yt[ct] = zero; }
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 ka = kt[(a * KS + s) * 64 + lane];
+                const uint4 qb = qt[(a * KS + s) * 64 + lane];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    X[ct] = mfma32(ka, Sb[ct][s], X[ct]);
+                    Yt[ct] = mfma32(Sb[ct][s], qb, Yt[ct]);
+                }
+            }
+            // R = beta (V - X); rows past the chunk's end are forced to zero
+            const float4 bb = *reinterpret_cast<const float4*>(&b.beta[16 * a + 4 * g]);
+            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int vc = 16 * CT * w + 16 * ct + li;
+                f32x4_t R;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * a + 4 * g + r;
+                    const unsigned char* vp = b.v + (row / VRP) * Buf::VPS + (row % VRP) * VRB + vc * ES;
+                    float vv;
+                    if constexpr (sizeof(TIn) == 2) vv = bf16_to_f32(*reinterpret_cast<const bf16_t*>(vp));
+                    else vv = *reinterpret_cast<const float*>(vp);
+                    R[r] = row < clen ? bv[r] * (vv - X[ct][r]) : 0.f;
+                }
+                Rb[a][ct] = pack_bf16x4(R);  // lane: R[16a + 4g + r][col li]
+            }
+            // U = T R (row tile a), O^T = Y^T + R^T M^T (token tile a).  The 16x16x16 chain
+            // starts from zero and Y^T is added on the VALU: an accumulator is never handed
+            // from a 16x16x32 product to a 16x16x16 one, a cross-shape dependency that the
+            // generated code did not always space far enough apart.
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4_t U = zero, Om = zero;
+#pragma unroll
+                for (int bq = 0; bq <= a; ++bq) {
+                    const int blk = tri_index(a, bq) * 64 + li * 4 + g;
+                    U = mfma16(tb[blk], Rb[bq][ct], U);
+                    Om = mfma16(Rb[bq][ct], mb[blk], Om);
+                }
+                const f32x4_t Ot = Om + Yt[ct];
+                Ub[a][ct] = pack_bf16x4(U);
+                // Ot[r] = O[16a + li][col0 + 16ct + 4g + r]
+                const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + (16 * ct + 4 * g) * ES;
+                if constexpr (sizeof(TIn) == 2) {
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])},
+                                                          ro, off, 0, 0);
+                } else {
+                    bstore16(ro, off, make_uint4(__float_as_uint(Ot[0]), __float_as_uint(Ot[1]),
+                                                 __float_as_uint(Ot[2]), __float_as_uint(Ot[3])));
+                }
             }
         }
-        if constexpr (sizeof(TIn) == 2) {
-            const uint4 o0 = *reinterpret_cast<const uint4*>(&sm.V[lane][16 * w]);
-            const uint4 o1 = *reinterpret_cast<const uint4*>(&sm.V[lane][16 * w + 8]);
-            bstore16(ro, lane * rowV, o0);
-            bstore16(ro, lane * rowV + 16, o1);
-        }
-        // ---- S = diag(e^{Gamma_n}) S + K^n^T U --------------------------------------------
+        // S = diag(e^{Gamma_n}) S + K^n^T U
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int s = m >> 1, hh = m & 1;
-            const float4 dn = *reinterpret_cast<const float4*>(&sm.decayN[32 * s + 8 * g + 4 * hh]);
-            Sacc[m][0] *= dn.x;
-            Sacc[m][1] *= dn.y;
-            Sacc[m][2] *= dn.z;
-            Sacc[m][3] *= dn.w;
-            const int krow = 32 * s + 8 * (li >> 2) + 4 * hh + (li & 3);  // pi(m, li)
+            const float4 dn = *reinterpret_cast<const float4*>(&dnv[32 * (m >> 1) + 8 * g + 4 * (m & 1)]);
+            const uint4 k0 = kn[(m * 2 + 0) * 64 + lane];
+            const uint4 k1 = kn[(m * 2 + 1) * 64 + lane];
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const uint2 a0 = *reinterpret_cast<const uint2*>(&sm.KnT[krow][32 * sp + 4 * g]);
-                const uint2 a1 = *reinterpret_cast<const uint2*>(&sm.KnT[krow][32 * sp + 16 + 4 * g]);
-                Sacc[m] = mfma32(make_uint4(a0.x, a0.y, a1.x, a1.y),
-                                 make_uint4(Ub[2 * sp].x, Ub[2 * sp].y, Ub[2 * sp + 1].x, Ub[2 * sp + 1].y),
-                                 Sacc[m]);
+            for (int ct = 0; ct < CT; ++ct) {
+                Sacc[ct][m][0] *= dn.x;
+                Sacc[ct][m][1] *= dn.y;
+                Sacc[ct][m][2] *= dn.z;
+                Sacc[ct][m][3] *= dn.w;
+                Sacc[ct][m] = mfma32(k0, make_uint4(Ub[0][ct].x, Ub[0][ct].y, Ub[1][ct].x, Ub[1][ct].y), Sacc[ct][m]);
+                Sacc[ct][m] = mfma32(k1, make_uint4(Ub[2][ct].x, Ub[2][ct].y, Ub[3][ct].x, Ub[3][ct].y), Sacc[ct][m]);
             }
         }
+        lds_barrier();
     }
 
     if (args.sN) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                args.sN[sbase + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] = Sacc[m][r];
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    args.sN[sbase + 16 * ct + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] =
+                        Sacc[ct][m][r];
     }
 }
 
@@ -708,7 +733,7 @@ size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk) {
     return table + static_cast<size_t>(split_max_chunks(total, n_seqs)) * H * split_block_bytes(dk);
 }
 
-template <int DK, int NW, typename TIn>
+template <int DK, int CT, typename TIn>
 static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
     SplitArgs a = a0;
     if (a.cu) {
@@ -724,21 +749,20 @@ static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    a.nslices = DK / (16 * NW);
+    a.nslices = DK / (64 * CT);
     const int groups = (a.npairs + 7) / 8;
-    hipLaunchKernelGGL((prefill_state_kernel<DK, NW, TIn>), dim3(static_cast<unsigned>(groups) * 8u * a.nslices),
-                       dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_state_kernel<DK, CT, TIn>), dim3(static_cast<unsigned>(groups) * 8u * a.nslices),
+                       dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int waves, hipStream_t stream) {
+hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ct, hipStream_t stream) {
     if (dk == 128) {
-        if (waves == 8) return bf16 ? launch_split_t<128, 8, bf16_t>(a, stream) : launch_split_t<128, 8, float>(a, stream);
-        if (waves == 2) return bf16 ? launch_split_t<128, 2, bf16_t>(a, stream) : launch_split_t<128, 2, float>(a, stream);
-        return bf16 ? launch_split_t<128, 4, bf16_t>(a, stream) : launch_split_t<128, 4, float>(a, stream);
+        // fp32 v rows of 128 columns would not fit two LDS stages: fp32 uses slices of 64
+        if (ct == 2 && bf16) return launch_split_t<128, 2, bf16_t>(a, stream);
+        return bf16 ? launch_split_t<128, 1, bf16_t>(a, stream) : launch_split_t<128, 1, float>(a, stream);
     }
-    if (waves == 2) return bf16 ? launch_split_t<64, 2, bf16_t>(a, stream) : launch_split_t<64, 2, float>(a, stream);
-    return bf16 ? launch_split_t<64, 4, bf16_t>(a, stream) : launch_split_t<64, 4, float>(a, stream);
+    return bf16 ? launch_split_t<64, 1, bf16_t>(a, stream) : launch_split_t<64, 1, float>(a, stream);
 }
 
 }  // namespace kda
