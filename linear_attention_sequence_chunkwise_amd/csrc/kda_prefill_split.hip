@@ -186,12 +186,12 @@ struct IntraSmem {
     float colscale[7][DK];
     float beta[kC];
     float Ld[4][16][20];       // diagonal blocks of A_kk (fp32), [block][col j][row i]
-    bf16_t L[kC][TROW];        // A_kk row-major (off-diagonal blocks)
-    bf16_t Aqk[kC][TROW];      // A_qk row-major (lower blocks, diagonal included)
+    bf16_t L[10][16][16];      // A_kk lower 16x16 blocks (off-diagonal ones used), row-major
+    bf16_t Aqk[10][16][16];    // A_qk lower blocks, diagonal included
 };
 
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
+__global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
     using Smem = IntraSmem<DK>;
     using P = Pair<TIn>;
     using B = Block<DK>;
@@ -385,12 +385,12 @@ __global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
                     sm.Ld[a][jj][li] = jj < li ? bi * ckk[r] : 0.f;  // strictly lower
                     qv[r] = jj <= li ? cqk[r] : 0.f;                // lower incl. diagonal
                 }
-                *reinterpret_cast<uint2*>(&sm.Aqk[16 * a + li][16 * b + 4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.Aqk[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
             } else {
-                *reinterpret_cast<uint2*>(&sm.L[16 * a + li][16 * b + 4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.L[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(bi * ckk[0], bi * ckk[1]), pack_bf16x2(bi * ckk[2], bi * ckk[3]));
-                *reinterpret_cast<uint2*>(&sm.Aqk[16 * a + li][16 * b + 4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.Aqk[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(cqk[0], cqk[1]), pack_bf16x2(cqk[2], cqk[3]));
             }
         }
@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
         for (int a = b + 1; a < 4; ++a) {
             f32x4_t acc = zero;
             for (int m = b; m < a; ++m)
-                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.L[16 * a + li][16 * m + 4 * g]),
+                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.L[tri_index(a, m)][li][4 * g]),
                              *reinterpret_cast<const uint2*>(&sm.u.out.Tt[16 * b + li][16 * m + 4 * g]), acc);
             const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.u.out.T[16 * a + li][16 * a + 4 * g]),
                                        pack_bf16x4(acc), zero);
@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(256) prefill_intra_kernel(SplitArgs args) {
             const int b = job - (a * (a + 1)) / 2;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             for (int m = b; m <= a; ++m)
-                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.Aqk[16 * a + li][16 * m + 4 * g]),
+                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.Aqk[tri_index(a, m)][li][4 * g]),
                              *reinterpret_cast<const uint2*>(&sm.u.out.Tt[16 * b + li][16 * m + 4 * g]), acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.u.out.M[16 * a + 4 * g + r][16 * b + li] = f32_to_bf16(acc[r]);
