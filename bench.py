@@ -59,9 +59,10 @@ def kernel_source_hash() -> str:
 
 
 def read_traffic(workload: str):
-    """HBM traffic per launch measured by rocprofv3 counters, if a summary for the current
-    kernel sources exists under profiles/ (else None)."""
-    path = os.path.join(ROOT, "profiles", f"prefill_chain_{workload}_traffic.txt")
+    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the same counter reads for a device copy of known size), if a summary for
+    the current kernel sources exists under profiles/ (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -131,6 +132,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before the timed "
+                         "region (a known-size reference for HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -146,6 +150,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kda.load_library()
+    if args.calibration_copy_mib > 0:
+        src = torch.ones(args.calibration_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     name = args.workload or workloads.PREFILL_B1
     inp = workloads.make(name)
     dev = lambda t: None if t is None else t.cuda()
@@ -204,7 +215,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic,
-                     "kernel": "prefill_chain_kernel", "avg_launch_ms": ms_event,
+                     "kernel": "kda_prefill_fwd (one call: chunk table, intra-chunk and "
+                               "state-pass kernels)", "avg_launch_ms": ms_event,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma_util": {"useful_tflops": mfma_tflops, "peak_tflops": BF16_PEAK_TFLOPS,
                       "frac": mfma_tflops / BF16_PEAK_TFLOPS,
@@ -256,7 +268,7 @@ def bench_decode(n_steps: int, distinct: int = 32, repeats: int = 3):
     return {"workload": workloads.DECODE, "steps": n_steps, "tokens_per_s": d.N * n_steps / t,
             "us_per_step": per_step * 1e6, "hbm_GBps": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": read_traffic(workloads.DECODE),
                          "kernel": "decode_kernel", "algorithmic_bytes_per_launch": byts},
             "inputs": f"{distinct} distinct seeded steps cycled"}
 

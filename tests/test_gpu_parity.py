@@ -68,7 +68,8 @@ def test_prefill_stress_gates(z_mean):
 
 
 def test_prefill_eight_wave_path():
-    """>= 256 (sequence, head) chains selects one 128-wide dv slice per workgroup."""
+    """More (sequence, head) chains than half the compute units selects one state-pass
+    workgroup covering all 128 dv columns (two 16-column tiles per compute wave)."""
     inp = workloads.prefill_inputs([80] * 16, H=16, dk=128, dv=128, dtype="bf16", seed=12,
                                    s0_std=0.02, name="n16_h16_t80")
     _check_prefill(inp, use_cu=False)
