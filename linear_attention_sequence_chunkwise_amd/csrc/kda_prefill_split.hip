@@ -621,92 +621,129 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
         const int64_t t0 = tok0 + static_cast<int64_t>(c) * kC;
         const rsrc_t ro = make_rsrc(obase + t0 * rowV, clen * rowV);
 
-        uint4 Sb[CT][KS];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct) {
+        f32x4_t* S = Sacc[ct];
+        const int vc = 16 * CT * w + 16 * ct + li;  // this lane's v column in the slice
+        uint4 Sb[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                Sb[ct][s] = make_uint4(pack_bf16x2(Sacc[ct][2 * s][0], Sacc[ct][2 * s][1]),
-                                       pack_bf16x2(Sacc[ct][2 * s][2], Sacc[ct][2 * s][3]),
-                                       pack_bf16x2(Sacc[ct][2 * s + 1][0], Sacc[ct][2 * s + 1][1]),
-                                       pack_bf16x2(Sacc[ct][2 * s + 1][2], Sacc[ct][2 * s + 1][3]));
-        uint2 Rb[4][CT], Ub[4][CT];
+        for (int s = 0; s < KS; ++s)
+            Sb[s] = make_uint4(pack_bf16x2(S[2 * s][0], S[2 * s][1]), pack_bf16x2(S[2 * s][2], S[2 * s][3]),
+                               pack_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]),
+                               pack_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]));
+        // The four token tiles are independent until U, so every product below is written as
+        // four (or more) interleaved accumulation chains that keep the MFMA pipe busy.  Each
+        // phase first issues all its LDS operand reads into registers; a scheduling fence keeps
+        // them ahead of the MFMAs, so the waits on them are pipelined instead of one full LDS
+        // latency per product.
+        uint4 opd[4][KS];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) opd[a][s] = kt[(a * KS + s) * 64 + lane];
+        float vv[4][4];  // v[16a + 4g + r][col vc]
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * a + 4 * g + r;
+                const unsigned char* vp = b.v + (row / VRP) * Buf::VPS + (row % VRP) * VRB + vc * ES;
+                if constexpr (sizeof(TIn) == 2) vv[a][r] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(vp));
+                else vv[a][r] = *reinterpret_cast<const float*>(vp);
+            }
+        float4 bb[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) bb[a] = *reinterpret_cast<const float4*>(&b.beta[16 * a + 4 * g]);
+        __builtin_amdgcn_sched_barrier(0);
+        // X = K~ S: X[a][r] = X[16a + 4g + r][col li]
+        f32x4_t X[4] = {zero, zero, zero, zero};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) X[a] = mfma32(opd[a][s], Sb[s], X[a]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) opd[a][s] = qt[(a * KS + s) * 64 + lane];
+        uint2 tv[10], mv[10];
+#pragma unroll
+        for (int t = 0; t < 10; ++t) {
+            tv[t] = tb[t * 64 + li * 4 + g];
+            mv[t] = mb[t * 64 + li * 4 + g];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Y^T = S^T Q~^T (independent of X; the R arithmetic below fills its MFMA latency)
+        f32x4_t Yt[4] = {zero, zero, zero, zero};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Yt[a] = mfma32(Sb[s], opd[a][s], Yt[a]);
+        // R = beta (V - X).  Rows past the chunk's end are zero without a test: the v copy
+        // writes zeros there, beta reads as zero, and K~ rows are zero, so X is zero too.
+        uint2 Rb[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            // X = K~ S (rows: tokens 4g + r of tile a), Y^T = S^T Q~^T (rows: columns 4g + r)
-            f32x4_t X[CT], Yt[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) { X[ct] = zero; Yt[ct] = zero; }
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint4 ka = kt[(a * KS + s) * 64 + lane];
-                const uint4 qb = qt[(a * KS + s) * 64 + lane];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    X[ct] = mfma32(ka, Sb[ct][s], X[ct]);
-                    Yt[ct] = mfma32(Sb[ct][s], qb, Yt[ct]);
-                }
-            }
-            // R = beta (V - X); rows past the chunk's end are forced to zero
-            const float4 bb = *reinterpret_cast<const float4*>(&b.beta[16 * a + 4 * g]);
-            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int vc = 16 * CT * w + 16 * ct + li;
-                f32x4_t R;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * a + 4 * g + r;
-                    const unsigned char* vp = b.v + (row / VRP) * Buf::VPS + (row % VRP) * VRB + vc * ES;
-                    float vv;
-                    if constexpr (sizeof(TIn) == 2) vv = bf16_to_f32(*reinterpret_cast<const bf16_t*>(vp));
-                    else vv = *reinterpret_cast<const float*>(vp);
-                    R[r] = row < clen ? bv[r] * (vv - X[ct][r]) : 0.f;
-                }
-                Rb[a][ct] = pack_bf16x4(R);  // lane: R[16a + 4g + r][col li]
-            }
-            // U = T R (row tile a), O^T = Y^T + R^T M^T (token tile a).  The 16x16x16 chain
-            // starts from zero and Y^T is added on the VALU: an accumulator is never handed
-            // from a 16x16x32 product to a 16x16x16 one, a cross-shape dependency that the
-            // generated code did not always space far enough apart.
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4_t U = zero, Om = zero;
-#pragma unroll
-                for (int bq = 0; bq <= a; ++bq) {
-                    const int blk = tri_index(a, bq) * 64 + li * 4 + g;
-                    U = mfma16(tb[blk], Rb[bq][ct], U);
-                    Om = mfma16(Rb[bq][ct], mb[blk], Om);
-                }
-                const f32x4_t Ot = Om + Yt[ct];
-                Ub[a][ct] = pack_bf16x4(U);
-                // Ot[r] = O[16a + li][col0 + 16ct + 4g + r]
-                const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + (16 * ct + 4 * g) * ES;
-                if constexpr (sizeof(TIn) == 2) {
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])},
-                                                          ro, off, 0, 0);
-                } else {
-                    bstore16(ro, off, make_uint4(__float_as_uint(Ot[0]), __float_as_uint(Ot[1]),
-                                                 __float_as_uint(Ot[2]), __float_as_uint(Ot[3])));
-                }
-            }
+            f32x4_t R;
+            R[0] = bb[a].x * (vv[a][0] - X[a][0]);
+            R[1] = bb[a].y * (vv[a][1] - X[a][1]);
+            R[2] = bb[a].z * (vv[a][2] - X[a][2]);
+            R[3] = bb[a].w * (vv[a][3] - X[a][3]);
+            Rb[a] = pack_bf16x4(R);  // lane: R[16a + 4g + r][col li]
         }
+        // U = T R and O^T = Y^T + R^T M^T, chains over the source tile b.  The M R chain starts
+        // from zero and Y^T is added on the VALU: an accumulator is never handed from a
+        // 16x16x32 product to a 16x16x16 one, a cross-shape dependency that the generated code
+        // did not always space far enough apart.
+        f32x4_t U[4] = {zero, zero, zero, zero}, Om[4] = {zero, zero, zero, zero};
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq)
+#pragma unroll
+            for (int a = bq; a < 4; ++a) {
+                const int t = tri_index(a, bq);
+                U[a] = mfma16(tv[t], Rb[bq], U[a]);
+                Om[a] = mfma16(Rb[bq], mv[t], Om[a]);
+            }
+        uint2 Ub[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) Ub[a] = pack_bf16x4(U[a]);
+        __builtin_amdgcn_sched_barrier(0);
         // S = diag(e^{Gamma_n}) S + K^n^T U
+        uint4 kk[2][MT];
+        float4 dn[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const float4 dn = *reinterpret_cast<const float4*>(&dnv[32 * (m >> 1) + 8 * g + 4 * (m & 1)]);
-            const uint4 k0 = kn[(m * 2 + 0) * 64 + lane];
-            const uint4 k1 = kn[(m * 2 + 1) * 64 + lane];
+            kk[0][m] = kn[(m * 2 + 0) * 64 + lane];
+            kk[1][m] = kn[(m * 2 + 1) * 64 + lane];
+            dn[m] = *reinterpret_cast<const float4*>(&dnv[32 * (m >> 1) + 8 * g + 4 * (m & 1)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                Sacc[ct][m][0] *= dn.x;
-                Sacc[ct][m][1] *= dn.y;
-                Sacc[ct][m][2] *= dn.z;
-                Sacc[ct][m][3] *= dn.w;
-                Sacc[ct][m] = mfma32(k0, make_uint4(Ub[0][ct].x, Ub[0][ct].y, Ub[1][ct].x, Ub[1][ct].y), Sacc[ct][m]);
-                Sacc[ct][m] = mfma32(k1, make_uint4(Ub[2][ct].x, Ub[2][ct].y, Ub[3][ct].x, Ub[3][ct].y), Sacc[ct][m]);
+        for (int m = 0; m < MT; ++m) {
+            S[m][0] *= dn[m].x;
+            S[m][1] *= dn[m].y;
+            S[m][2] *= dn[m].z;
+            S[m][3] *= dn[m].w;
+        }
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                S[m] = mfma32(kk[sp][m], make_uint4(Ub[2 * sp].x, Ub[2 * sp].y, Ub[2 * sp + 1].x, Ub[2 * sp + 1].y), S[m]);
+        // O: Ot[r] = O[16a + li][col0 + 16ct + 4g + r]
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4_t Ot = Om[a] + Yt[a];
+            const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + (16 * ct + 4 * g) * ES;
+            if constexpr (sizeof(TIn) == 2) {
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])},
+                                                      ro, off, 0, 0);
+            } else {
+                bstore16(ro, off, make_uint4(__float_as_uint(Ot[0]), __float_as_uint(Ot[1]),
+                                             __float_as_uint(Ot[2]), __float_as_uint(Ot[3])));
             }
         }
+        }  // column tile
         lds_barrier();
     }
 
