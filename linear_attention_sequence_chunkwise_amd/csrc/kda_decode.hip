@@ -7,8 +7,10 @@
 //
 // The step is bound by HBM traffic: each (sequence, head) streams its dk x dv fp32 state
 // in and back out (128 KiB at d = 128) against a few hundred bytes of inputs.  One
-// workgroup of 256 threads owns one (sequence, head); each thread keeps RPT rows x 4
-// columns of the state in registers (16-byte loads/stores along dv, coalesced).  Both
+// workgroup of NT threads (1024 at d = 128) owns one (sequence, head); each thread keeps
+// RPT rows x 4 columns of the state in registers (16-byte loads/stores along dv, coalesced,
+// marked nontemporal: the state is touched once per step).  Small per-thread tiles keep
+// many state loads in flight per CU, which is what sustains the bandwidth.  Both
 // reductions over key channels happen in one pass because
 //   o = S_t^T q = Sbar^T q + (k.q) beta (v - Sbar^T k),
 // so the state is read once, updated in registers, and written once.
@@ -17,14 +19,13 @@
 
 namespace kda {
 
-template <int D, typename TIn>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs args) {
-    constexpr int NT = 256;
+template <int D, int NT, typename TIn>
+__global__ void __launch_bounds__(NT) decode_kernel(DecodeArgs args) {
     constexpr int COLG = D / 4;         // float4 column groups
     constexpr int ROWG = NT / COLG;     // row groups
     constexpr int RPT = D / ROWG;       // rows per thread
     constexpr int NWV = NT / 64;        // waves
-    constexpr int RG_PER_WAVE = 64 / COLG;
+    static_assert(NT % COLG == 0 && D % ROWG == 0 && COLG <= 64 && D <= NT, "thread tiling");
 
     __shared__ float s_alpha[D], s_k[D], s_q[D], s_u[D];
     __shared__ float s_red[NWV][2][D];
@@ -51,10 +52,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs args) {
     }
     // state tile of this thread: rows rg + ROWG*i, columns 4cg .. 4cg+3
     const int cg = tid % COLG, rg = tid / COLG;
-    float4* __restrict__ st = reinterpret_cast<float4*>(args.state + static_cast<size_t>(pair) * D * D);
+    f32x4_t* __restrict__ st = reinterpret_cast<f32x4_t*>(args.state + static_cast<size_t>(pair) * D * D);
     float4 S[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = st[(rg + ROWG * i) * COLG + cg];
+    for (int i = 0; i < RPT; ++i) {
+        const f32x4_t t = __builtin_nontemporal_load(&st[(rg + ROWG * i) * COLG + cg]);
+        S[i] = make_float4(t[0], t[1], t[2], t[3]);
+    }
 
     // k.q: wave reduction, then across waves
 #pragma unroll
@@ -105,19 +109,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs args) {
     for (int i = 0; i < RPT; ++i) {
         const float kr = s_k[rg + ROWG * i];
         S[i].x += kr * u4.x; S[i].y += kr * u4.y; S[i].z += kr * u4.z; S[i].w += kr * u4.w;
-        st[(rg + ROWG * i) * COLG + cg] = S[i];
+        __builtin_nontemporal_store(f32x4_t{S[i].x, S[i].y, S[i].z, S[i].w}, &st[(rg + ROWG * i) * COLG + cg]);
     }
-    (void)RG_PER_WAVE;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H));
     if (d == 128) {
-        if (bf16) hipLaunchKernelGGL((decode_kernel<128, bf16_t>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<128, float>), grid, dim3(256), 0, stream, a);
+        if (bf16) hipLaunchKernelGGL((decode_kernel<128, 1024, bf16_t>), grid, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<128, 1024, float>), grid, dim3(1024), 0, stream, a);
     } else {
-        if (bf16) hipLaunchKernelGGL((decode_kernel<64, bf16_t>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<64, float>), grid, dim3(256), 0, stream, a);
+        if (bf16) hipLaunchKernelGGL((decode_kernel<64, 512, bf16_t>), grid, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<64, 512, float>), grid, dim3(512), 0, stream, a);
     }
     return hipGetLastError();
 }
