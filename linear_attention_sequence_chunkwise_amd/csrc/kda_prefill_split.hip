@@ -75,15 +75,6 @@ __device__ __forceinline__ uint32_t kn_off(int c, int t4) {
     return static_cast<uint32_t>(((m * 2 + (t4 >> 5)) * 64 + ((u & 15) >> 2) * 16 + li) * 16 + (u >> 4) * 8);
 }
 
-// Column-operand scale index of tile pair (a, b): -1 means 1.
-__device__ __forceinline__ int colscale_index(int a, int b) {
-    if (a == b) return a;
-    if (a == 2 && b == 0) return 4;
-    if (a == 3 && b == 0) return 5;
-    if (a == 3 && b == 1) return 6;
-    return -1;
-}
-
 __device__ __forceinline__ uint4 scale8(uint4 x, float4 s0, float4 s1) {
     return make_uint4(pack_bf16x2(lo_bf16(x.x) * s0.x, hi_bf16(x.x) * s0.y),
                       pack_bf16x2(lo_bf16(x.y) * s0.z, hi_bf16(x.y) * s0.w),
@@ -99,6 +90,10 @@ template <> struct Pair<bf16_t> {
     struct Row8 { uint4 a; };
     __device__ __forceinline__ static Row8 load8(rsrc_t r, uint32_t off) { return Row8{bload16(r, off)}; }
     __device__ __forceinline__ static uint4 bf16x8(const Row8& x) { return x.a; }
+    __device__ __forceinline__ static float at(const Row8& x, int e) {
+        const uint32_t wv = e < 2 ? x.a.x : e < 4 ? x.a.y : e < 6 ? x.a.z : x.a.w;
+        return (e & 1) ? hi_bf16(wv) : lo_bf16(wv);
+    }
     __device__ __forceinline__ static float load_beta(rsrc_t r, uint32_t off) {
         return __uint_as_float(bload2(r, off) << 16);
     }
@@ -112,6 +107,11 @@ template <> struct Pair<float> {
     struct Row8 { uint4 a, b; };
     __device__ __forceinline__ static Row8 load8(rsrc_t r, uint32_t off) {
         return Row8{bload16(r, off), bload16(r, off + 16)};
+    }
+    __device__ __forceinline__ static float at(const Row8& x, int e) {
+        const uint4& u = e < 4 ? x.a : x.b;
+        const int i = e & 3;
+        return __uint_as_float(i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w);
     }
     __device__ __forceinline__ static uint4 bf16x8(const Row8& x) {
         return make_uint4(pack_bf16x2(__uint_as_float(x.a.x), __uint_as_float(x.a.y)),
@@ -164,45 +164,54 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* cu, in
 }
 
 // ---- K1: intra-chunk factors ------------------------------------------------------------
+// One workgroup of four waves per (chunk, head).  Wave w owns 16-token tile w and works in
+// the MFMA operand layout from the start: lane (g, li) holds token 16w + li and the channels
+// 32s + 8g .. 32s + 8g + 7 for every K-step s, exactly the 16 bytes per step it feeds to a
+// 16x16x32 product.  The cumulative decays within a tile are therefore an inclusive product
+// scan across the 16 lanes of a DPP row, K~ and Q~ leave registers as linear 1 KiB lane-order
+// writes, and only the column operands (read by other waves) and K^n (transposed for the
+// state pass) go through LDS.
 template <int DK>
 struct IntraSmem {
-    static constexpr int NT = 256;
-    static constexpr int KROW = DK + 16;      // 16-byte operand reads over 16 rows: no conflict
-    static constexpr int TROW = kC + 8;
-    static constexpr int SEG = 32 * DK / NT;  // gate item: SEG tokens x 2 channels
-    static constexpr int NSEG = kC / SEG;
-    struct Ops {
-        bf16_t Kr[kC][KROW];   // k_i e^{Gamma_i - rho_a}
-        bf16_t Qr[kC][KROW];   // q_i e^{Gamma_i - rho_a}
-        bf16_t Kc[kC][KROW];   // k_j e^{rho_{b+1} - Gamma_j}
-    };
+    static constexpr int KS = DK / 32;
+    static constexpr int NROW = DK + 8;  // K^n staging rows (bf16), 16-byte aligned
     struct Out {
-        bf16_t T[kC][TROW];    // T, row-major
-        bf16_t Tt[kC][TROW];   // T transposed
-        bf16_t M[kC][TROW];    // M = A_qk T, row-major
+        bf16_t T[10][16][16];   // T lower 16x16 blocks, row-major
+        bf16_t Tt[10][16][16];  // the same blocks transposed
+        bf16_t M[10][16][16];   // M = A_qk T lower blocks, row-major
     };
-    union { Ops ops; Out out; } u;
-    float Pseg[NSEG][DK];
-    float colscale[7][DK];
+    uint4 kc[4 * KS * 64];      // k_j e^{rho_{b+1} - Gamma_j} in lane order [b][s][lane]
+    union { bf16_t kn[kC][NROW]; Out out; } u;  // K^n = K e^{Gamma_n - Gamma} (token-major), later T, M
+    float ttile[4][DK];         // e^{rho_{a+1} - rho_a}: the product of alpha over tile a
+    float ae[DK];               // -e^{A} log2(e)
     float beta[kC];
-    float Ld[4][16][20];       // diagonal blocks of A_kk (fp32), [block][col j][row i]
-    bf16_t L[10][16][16];      // A_kk lower 16x16 blocks (off-diagonal ones used), row-major
-    bf16_t Aqk[10][16][16];    // A_qk lower blocks, diagonal included
+    float Ld[4][16][20];        // diagonal blocks of A_kk (fp32), [block][col j][row i]
+    bf16_t L[10][16][16];       // A_kk lower blocks (off-diagonal ones used), row-major
+    bf16_t Aqk[10][16][16];     // A_qk lower blocks, diagonal included
 };
 
+// x[lane - n] within the lane's row of 16, or 1 for the first n lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shr_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x110 | N, 0xf, 0xf,
+                                                      false));
+}
+
+__device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
+    const uint4& u = e < 4 ? a : b;
+    const int i = e & 3;
+    return __uint_as_float(i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w);
+}
+
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
+__global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_kernel(SplitArgs args) {
     using Smem = IntraSmem<DK>;
     using P = Pair<TIn>;
     using B = Block<DK>;
-    constexpr int NT = Smem::NT;
-    constexpr int SEG = Smem::SEG;
-    constexpr int NSEG = Smem::NSEG;
-    constexpr int SPT = 16 / SEG;
-    constexpr int NCP = DK / 2;
-    constexpr int KSTEPS = DK / 32;
+    constexpr int NT = 256;
+    constexpr int KS = DK / 32;
+    constexpr int MT = DK / 16;
     constexpr int ES = static_cast<int>(sizeof(TIn));
-    static_assert(NSEG * NCP == NT && (SEG == 8 || SEG == 16), "items");
 
     __shared__ Smem sm;
     const int tid = threadIdx.x;
@@ -238,152 +247,193 @@ __global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
     const char* qbase = static_cast<const char*>(args.q) + static_cast<size_t>(h) * DK * ES;
     const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
     const char* zbase = reinterpret_cast<const char*>(args.z) + static_cast<size_t>(h) * DK * 4;
-
-    // gate item: segment iseg (tokens SEG*iseg ..), channels ch0, ch0 + 1
-    const int icp = tid % NCP, iseg = tid / NCP, ch0 = 2 * icp;
-    const int itile = iseg / SPT, isub = iseg % SPT;
-    const float ae0 = -expf(args.A[h * DK + ch0]) * kLog2e;  // -e^{A} log2(e)
-    const float ae1 = -expf(args.A[h * DK + ch0 + 1]) * kLog2e;
     const float gscale = args.g_min * kLog2e;
 
-    // ---- loads (rows past the sequence end read as zero) --------------------------------
-    typename P::raw pk[SEG], pq[SEG];
-    uint2 pz[SEG];
+    // ---- loads: this lane's token r and channels 32s + 8g .. (rows past the end read 0) ----
+    const int r = 16 * w + li;
+    typename P::Row8 pk[KS], pq[KS];
+    uint4 pz[KS][2];
     {
         const rsrc_t rk = make_rsrc(kbase + t0 * rowK, clen * rowK);
         const rsrc_t rq = make_rsrc(qbase + t0 * rowK, clen * rowK);
         const rsrc_t rz = make_rsrc(zbase + t0 * rowZ, clen * rowZ);
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) {
-            const uint32_t row = static_cast<uint32_t>(iseg * SEG + i);
-            pk[i] = P::load(rk, row * rowK + ch0 * ES);
-            pq[i] = P::load(rq, row * rowK + ch0 * ES);
-            pz[i] = bload8(rz, row * rowZ + ch0 * 4);
+        for (int s = 0; s < KS; ++s) {
+            const uint32_t ch = 32 * s + 8 * g;
+            pk[s] = P::load8(rk, r * rowK + ch * ES);
+            pq[s] = P::load8(rq, r * rowK + ch * ES);
+            pz[s][0] = bload16(rz, r * rowZ + ch * 4);
+            pz[s][1] = bload16(rz, r * rowZ + ch * 4 + 16);
         }
+        if (tid < DK) sm.ae[tid] = -expf(args.A[h * DK + tid]) * kLog2e;
         if (tid < kC) {
             const rsrc_t rb = make_rsrc(bbase + t0 * rowB, clen * rowB);
             sm.beta[tid] = P::load_beta(rb, tid * rowB);
         }
     }
+    lds_barrier();
 
-    // ---- gates: alpha = e^g, tokens past the end get alpha = 1 (g = 0) -----------------------
-    float2 al[SEG];
+    // ---- gates alpha = e^g (tokens past the end: alpha = 1), then F = e^{Gamma_i - rho_w}:
+    // an inclusive product scan over the 16 tokens of the tile (lanes li of one row) ---------
+    float F[KS][8];
     {
-        float2 Pq = make_float2(1.f, 1.f);
+        const bool valid = r < clen;
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) {
-            const bool valid = iseg * SEG + i < clen;
-            const float s0 = fast_rcp(1.f + fast_exp2(ae0 * __uint_as_float(pz[i].x)));
-            const float s1 = fast_rcp(1.f + fast_exp2(ae1 * __uint_as_float(pz[i].y)));
-            al[i].x = valid ? fast_exp2(gscale * s0) : 1.f;
-            al[i].y = valid ? fast_exp2(gscale * s1) : 1.f;
-            Pq.x *= al[i].x;
-            Pq.y *= al[i].y;
+        for (int s = 0; s < KS; ++s) {
+            const float4 a0 = *reinterpret_cast<const float4*>(&sm.ae[32 * s + 8 * g]);
+            const float4 a1 = *reinterpret_cast<const float4*>(&sm.ae[32 * s + 8 * g + 4]);
+            const float ae8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sg = fast_rcp(1.f + fast_exp2(ae8[e] * lane8(pz[s][0], pz[s][1], e)));
+                F[s][e] = valid ? fast_exp2(gscale * sg) : 1.f;
+            }
         }
-        *reinterpret_cast<float2*>(&sm.Pseg[iseg][ch0]) = Pq;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<1>(F[s][e]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<2>(F[s][e]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<4>(F[s][e]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<8>(F[s][e]);
+        if (li == 15) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                *reinterpret_cast<float4*>(&sm.ttile[w][32 * s + 8 * g]) = make_float4(F[s][0], F[s][1], F[s][2], F[s][3]);
+                *reinterpret_cast<float4*>(&sm.ttile[w][32 * s + 8 * g + 4]) = make_float4(F[s][4], F[s][5], F[s][6], F[s][7]);
+            }
+        }
     }
     lds_barrier();
 
-    // ---- operands: Kr, Qr, Kc to LDS; Kt, Qt, KnT, decayN to the factor block -----------
-    {
-        float2 ps[NSEG];
+    // ---- operands.  Row operands (registers): Kr = k e^{Gamma_i - rho_w}, Qr likewise.
+    // Column operand (LDS): k e^{rho_{w+1} - Gamma_i}.  Factor block: K~ = k e^{Gamma_i},
+    // Q~ = q e^{Gamma_i} (lane order, straight from registers), K^n staged for transposition.
+    uint4 kr[KS], qr[KS];
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) ps[s] = *reinterpret_cast<const float2*>(&sm.Pseg[s][ch0]);
-        float2 Tt[4];  // tile products e^{rho_{a+1} - rho_a}
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            Tt[a] = ps[a * SPT];
-            if (SPT == 2) { Tt[a].x *= ps[a * SPT + 1].x; Tt[a].y *= ps[a * SPT + 1].y; }
-        }
-        float2 eR = make_float2(1.f, 1.f), eN = eR;  // e^{rho_a}, e^{Gamma_n - rho_{a+1}}
+    for (int s = 0; s < KS; ++s) {
+        const int ch = 32 * s + 8 * g;
+        float Tt[4][8];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            if (a < itile) { eR.x *= Tt[a].x; eR.y *= Tt[a].y; }
-            if (a > itile) { eN.x *= Tt[a].x; eN.y *= Tt[a].y; }
+            const float4 x0 = *reinterpret_cast<const float4*>(&sm.ttile[a][ch]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&sm.ttile[a][ch + 4]);
+            Tt[a][0] = x0.x; Tt[a][1] = x0.y; Tt[a][2] = x0.z; Tt[a][3] = x0.w;
+            Tt[a][4] = x1.x; Tt[a][5] = x1.y; Tt[a][6] = x1.z; Tt[a][7] = x1.w;
         }
-        float2 pre = make_float2(1.f, 1.f), post = pre;
-        if (SPT == 2) {
-            const float2 other = *reinterpret_cast<const float2*>(&sm.Pseg[iseg ^ 1][ch0]);
-            if (isub == 1) pre = other;
-            else post = other;
-        }
-        float2 E[SEG];  // e^{rho_{a+1} - Gamma_i}
-        E[SEG - 1] = post;
+        float vkr[8], vqr[8], vkc[8], vkt[8], vqt[8], vkn[8], vdn[8];
 #pragma unroll
-        for (int i = SEG - 2; i >= 0; --i)
-            E[i] = make_float2(E[i + 1].x * al[i + 1].x, E[i + 1].y * al[i + 1].y);
-        float2 F = pre;  // e^{Gamma_i - rho_a}
-        float2 kn[SEG];
+        for (int e = 0; e < 8; ++e) {
+            float tw = Tt[0][e], eR = 1.f, eN = 1.f;
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) {
-            const int r = iseg * SEG + i;
-            F.x *= al[i].x;
-            F.y *= al[i].y;
-            const float2 kf = P::get(pk[i]), qf = P::get(pq[i]);
-            const float2 FR = make_float2(F.x * eR.x, F.y * eR.y);
-            *reinterpret_cast<uint32_t*>(&sm.u.ops.Kr[r][ch0]) = pack_bf16x2(kf.x * F.x, kf.y * F.y);
-            *reinterpret_cast<uint32_t*>(&sm.u.ops.Qr[r][ch0]) = pack_bf16x2(qf.x * F.x, qf.y * F.y);
-            *reinterpret_cast<uint32_t*>(&sm.u.ops.Kc[r][ch0]) = pack_bf16x2(kf.x * E[i].x, kf.y * E[i].y);
-            *reinterpret_cast<uint32_t*>(blk + B::KT + lane_off<DK>(r, ch0)) = pack_bf16x2(kf.x * FR.x, kf.y * FR.y);
-            *reinterpret_cast<uint32_t*>(blk + B::QT + lane_off<DK>(r, ch0)) = pack_bf16x2(qf.x * FR.x, qf.y * FR.y);
-            kn[i] = make_float2(kf.x * (E[i].x * eN.x), kf.y * (E[i].y * eN.y));
-        }
+            for (int a = 1; a < 4; ++a) tw = w == a ? Tt[a][e] : tw;
 #pragma unroll
-        for (int j = 0; j < SEG / 4; ++j) {
-            const int tk = iseg * SEG + 4 * j;
-            *reinterpret_cast<uint2*>(blk + B::KN + kn_off(ch0, tk)) =
-                make_uint2(pack_bf16x2(kn[4 * j].x, kn[4 * j + 1].x), pack_bf16x2(kn[4 * j + 2].x, kn[4 * j + 3].x));
-            *reinterpret_cast<uint2*>(blk + B::KN + kn_off(ch0 + 1, tk)) =
-                make_uint2(pack_bf16x2(kn[4 * j].y, kn[4 * j + 1].y), pack_bf16x2(kn[4 * j + 2].y, kn[4 * j + 3].y));
+            for (int a = 0; a < 4; ++a) {
+                eR *= a < w ? Tt[a][e] : 1.f;
+                eN *= a > w ? Tt[a][e] : 1.f;
+            }
+            const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
+            const float f = F[s][e];
+            const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
+            vkr[e] = kf * f;
+            vqr[e] = qf * f;
+            vkc[e] = kf * E;
+            vkt[e] = vkr[e] * eR;
+            vqt[e] = vqr[e] * eR;
+            vkn[e] = vkc[e] * eN;
+            vdn[e] = Tt[0][e] * Tt[1][e] * Tt[2][e] * Tt[3][e];
         }
-        if (iseg == 0) {
+        kr[s] = make_uint4(pack_bf16x2(vkr[0], vkr[1]), pack_bf16x2(vkr[2], vkr[3]), pack_bf16x2(vkr[4], vkr[5]),
+                           pack_bf16x2(vkr[6], vkr[7]));
+        qr[s] = make_uint4(pack_bf16x2(vqr[0], vqr[1]), pack_bf16x2(vqr[2], vqr[3]), pack_bf16x2(vqr[4], vqr[5]),
+                           pack_bf16x2(vqr[6], vqr[7]));
+        const int piece = (w * KS + s) * 64 + lane;
+        sm.kc[piece] = make_uint4(pack_bf16x2(vkc[0], vkc[1]), pack_bf16x2(vkc[2], vkc[3]),
+                                  pack_bf16x2(vkc[4], vkc[5]), pack_bf16x2(vkc[6], vkc[7]));
+        *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) =
+            make_uint4(pack_bf16x2(vkt[0], vkt[1]), pack_bf16x2(vkt[2], vkt[3]), pack_bf16x2(vkt[4], vkt[5]),
+                       pack_bf16x2(vkt[6], vkt[7]));
+        *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) =
+            make_uint4(pack_bf16x2(vqt[0], vqt[1]), pack_bf16x2(vqt[2], vqt[3]), pack_bf16x2(vqt[4], vqt[5]),
+                       pack_bf16x2(vqt[6], vqt[7]));
+        *reinterpret_cast<uint4*>(&sm.u.kn[r][ch]) =
+            make_uint4(pack_bf16x2(vkn[0], vkn[1]), pack_bf16x2(vkn[2], vkn[3]), pack_bf16x2(vkn[4], vkn[5]),
+                       pack_bf16x2(vkn[6], vkn[7]));
+        if (w == 0 && li == 0) {
+            *reinterpret_cast<float4*>(blk + B::DN + ch * 4) = make_float4(vdn[0], vdn[1], vdn[2], vdn[3]);
+            *reinterpret_cast<float4*>(blk + B::DN + ch * 4 + 16) = make_float4(vdn[4], vdn[5], vdn[6], vdn[7]);
+        }
+    }
+    lds_barrier();
+
+    // ---- K^n^T in lane order: piece (m, sp, lane) holds, for lane (g, li), the tokens
+    // 32sp + 4g .. and 32sp + 16 + 4g .. of channel pi(m, li) ------------------------------
+    for (int p = tid; p < MT * 2 * 64; p += NT) {
+        const int m = p >> 7, sp = (p >> 6) & 1, pl = p & 63, pg = pl >> 4, pli = pl & 15;
+        const int c = 32 * (m >> 1) + 8 * (pli >> 2) + 4 * (m & 1) + (pli & 3);
+        const int ta = 32 * sp + 4 * pg;
+        uint32_t wv[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const float T0 = e ? Tt[0].y : Tt[0].x, T1 = e ? Tt[1].y : Tt[1].x;
-                const float T2 = e ? Tt[2].y : Tt[2].x, T3 = e ? Tt[3].y : Tt[3].x;
-                const int c = ch0 + e;
-                sm.colscale[0][c] = fast_rcp(T0);
-                sm.colscale[1][c] = fast_rcp(T1);
-                sm.colscale[2][c] = fast_rcp(T2);
-                sm.colscale[3][c] = fast_rcp(T3);
-                sm.colscale[4][c] = T1;
-                sm.colscale[5][c] = T1 * T2;
-                sm.colscale[6][c] = T2;
+                const int t = ta + 16 * hh + 2 * e;
+                wv[2 * hh + e] = static_cast<uint32_t>(sm.u.kn[t][c]) | (static_cast<uint32_t>(sm.u.kn[t + 1][c]) << 16);
             }
-            *reinterpret_cast<float2*>(blk + B::DN + ch0 * 4) =
-                make_float2(Tt[0].x * Tt[1].x * Tt[2].x * Tt[3].x, Tt[0].y * Tt[1].y * Tt[2].y * Tt[3].y);
-        }
+        *reinterpret_cast<uint4*>(blk + B::KN + p * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
-    lds_barrier();
 
-    // ---- lower 16x16 tiles of A_kk and A_qk (transposed product: lane ends with four
-    // consecutive columns j of one row i) -----------------------------------------------
-#pragma unroll
-    for (int slot2 = 0; slot2 < 3; ++slot2) {
-        const int job = w + slot2 * 4;
-        if (job < 10) {
-            const int a = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-            const int b = job - (a * (a + 1)) / 2;
-            const int si = colscale_index(a, b);
+    // ---- lower 16x16 tiles (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
+    // carries e^{rho_{b+1} - Gamma_j}; it is rescaled per channel by e^{rho_w - rho_{b+1}}
+    // (the reciprocal of tile w's own product on the diagonal, at most e^80).  Transposed
+    // product: lane ends with four consecutive columns j of one row i.
+    {
+        const float bi = sm.beta[r];
+        for (int b = 0; b <= w; ++b) {
             f32x4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
+            for (int s = 0; s < KS; ++s) {
                 const int ch = 32 * s + 8 * g;
-                uint4 col = *reinterpret_cast<const uint4*>(&sm.u.ops.Kc[16 * b + li][ch]);
-                if (si >= 0)
-                    col = scale8(col, *reinterpret_cast<const float4*>(&sm.colscale[si][ch]),
-                                 *reinterpret_cast<const float4*>(&sm.colscale[si][ch + 4]));
-                ckk = mfma32(col, *reinterpret_cast<const uint4*>(&sm.u.ops.Kr[16 * a + li][ch]), ckk);
-                cqk = mfma32(col, *reinterpret_cast<const uint4*>(&sm.u.ops.Qr[16 * a + li][ch]), cqk);
+                uint4 col = sm.kc[(b * KS + s) * 64 + lane];
+                if (b != w - 1) {
+                    float4 s0, s1;
+                    if (b == w) {
+                        const float4 t0v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch]);
+                        const float4 t1v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4]);
+                        s0 = make_float4(fast_rcp(t0v.x), fast_rcp(t0v.y), fast_rcp(t0v.z), fast_rcp(t0v.w));
+                        s1 = make_float4(fast_rcp(t1v.x), fast_rcp(t1v.y), fast_rcp(t1v.z), fast_rcp(t1v.w));
+                    } else {
+                        s0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch]);
+                        s1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch + 4]);
+                        if (b == w - 3) {
+                            const float4 u0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch]);
+                            const float4 u1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch + 4]);
+                            s0 = make_float4(s0.x * u0.x, s0.y * u0.y, s0.z * u0.z, s0.w * u0.w);
+                            s1 = make_float4(s1.x * u1.x, s1.y * u1.y, s1.z * u1.z, s1.w * u1.w);
+                        }
+                    }
+                    col = scale8(col, s0, s1);
+                }
+                ckk = mfma32(col, kr[s], ckk);
+                cqk = mfma32(col, qr[s], cqk);
             }
-            const float bi = sm.beta[16 * a + li];
-            if (a == b) {
+            const int job = tri_index(w, b);
+            if (b == w) {
                 float qv[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jj = 4 * g + r;
-                    sm.Ld[a][jj][li] = jj < li ? bi * ckk[r] : 0.f;  // strictly lower
-                    qv[r] = jj <= li ? cqk[r] : 0.f;                // lower incl. diagonal
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int jj = 4 * g + rr;
+                    sm.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
+                    qv[rr] = jj <= li ? cqk[rr] : 0.f;                // lower incl. diagonal
                 }
                 *reinterpret_cast<uint2*>(&sm.Aqk[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
@@ -415,12 +465,13 @@ __global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
 #pragma unroll
             for (int i = m + 1; i < 16; ++i) t[i] -= Lm[i] * tm;
         }
-        // column j of T_aa -> T (row-major) and Tt (row j)
+        // column j of T_aa -> T block (row-major) and its transpose (row j)
+        const int d = tri_index(a, a);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.u.out.T[16 * a + i][16 * a + j] = f32_to_bf16(t[i]);
+        for (int i = 0; i < 16; ++i) sm.u.out.T[d][i][j] = f32_to_bf16(t[i]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<uint2*>(&sm.u.out.Tt[16 * a + j][16 * a + 4 * q4]) =
+            *reinterpret_cast<uint2*>(&sm.u.out.Tt[d][j][4 * q4]) =
                 make_uint2(pack_bf16x2(t[4 * q4], t[4 * q4 + 1]), pack_bf16x2(t[4 * q4 + 2], t[4 * q4 + 3]));
     }
     lds_barrier();
@@ -433,13 +484,14 @@ __global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
             f32x4_t acc = zero;
             for (int m = b; m < a; ++m)
                 acc = mfma16(*reinterpret_cast<const uint2*>(&sm.L[tri_index(a, m)][li][4 * g]),
-                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[16 * b + li][16 * m + 4 * g]), acc);
-            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.u.out.T[16 * a + li][16 * a + 4 * g]),
+                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[tri_index(m, b)][li][4 * g]), acc);
+            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.u.out.T[tri_index(a, a)][li][4 * g]),
                                        pack_bf16x4(acc), zero);
-            // tab[r] = -T_ab[4g + r][li]
+            // tab[rr] = -T_ab[4g + rr][li]
+            const int d = tri_index(a, b);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.u.out.T[16 * a + 4 * g + r][16 * b + li] = f32_to_bf16(-tab[r]);
-            *reinterpret_cast<uint2*>(&sm.u.out.Tt[16 * b + li][16 * a + 4 * g]) =
+            for (int rr = 0; rr < 4; ++rr) sm.u.out.T[d][4 * g + rr][li] = f32_to_bf16(-tab[rr]);
+            *reinterpret_cast<uint2*>(&sm.u.out.Tt[d][li][4 * g]) =
                 make_uint2(pack_bf16x2(-tab[0], -tab[1]), pack_bf16x2(-tab[2], -tab[3]));
         }
     }
@@ -455,23 +507,19 @@ __global__ void __launch_bounds__(256, 2) prefill_intra_kernel(SplitArgs args) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             for (int m = b; m <= a; ++m)
                 acc = mfma16(*reinterpret_cast<const uint2*>(&sm.Aqk[tri_index(a, m)][li][4 * g]),
-                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[16 * b + li][16 * m + 4 * g]), acc);
+                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[tri_index(m, b)][li][4 * g]), acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.u.out.M[16 * a + 4 * g + r][16 * b + li] = f32_to_bf16(acc[r]);
+            for (int rr = 0; rr < 4; ++rr) sm.u.out.M[job][4 * g + rr][li] = f32_to_bf16(acc[rr]);
         }
     }
     lds_barrier();
 
     // ---- T and M lower blocks -> factor block (512 bytes per block, 16-byte pieces) -------
     for (int idx = tid; idx < 2 * 10 * 32; idx += NT) {
-        const int which = idx / 320, rem = idx % 320, blk_i = rem / 32, piece = rem % 32;
-        const int a = blk_i < 1 ? 0 : blk_i < 3 ? 1 : blk_i < 6 ? 2 : 3;
-        const int b = blk_i - (a * (a + 1)) / 2;
-        const int row = piece >> 1, half = piece & 1;
-        const bf16_t* src = which == 0 ? &sm.u.out.T[16 * a + row][16 * b + 8 * half]
-                                       : &sm.u.out.M[16 * a + row][16 * b + 8 * half];
-        *reinterpret_cast<uint4*>(blk + (which == 0 ? B::TB : B::MB) + blk_i * 512 + row * 32 + half * 16) =
-            *reinterpret_cast<const uint4*>(src);
+        const int which = idx / 320, rem = idx % 320;
+        const uint4* src = which == 0 ? reinterpret_cast<const uint4*>(&sm.u.out.T[0][0][0])
+                                      : reinterpret_cast<const uint4*>(&sm.u.out.M[0][0][0]);
+        *reinterpret_cast<uint4*>(blk + (which == 0 ? B::TB : B::MB) + rem * 16) = src[rem];
     }
 }
 
