@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--checkpoint-interval", type=int, default=0,
+                    help="also write prefix-cache checkpoints every this many tokens "
+                         "(kda_prefill_fwd_checkpointed; 0 = off)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the timed "
                          "region (a known-size reference for HBM traffic counters)")
@@ -170,10 +173,19 @@ def main():
     ws = torch.empty(kda.kda_prefill_workspace_size(inp.total, inp.N, inp.H, inp.dk, inp.dv, q.dtype),
                      dtype=torch.uint8, device="cuda")
 
+    ck = ck_off = None
+    if args.checkpoint_interval > 0:
+        counts = [L // args.checkpoint_interval for L in inp.lengths]
+        offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        ck = torch.empty((max(1, int(offs[-1])), inp.H, inp.dk, inp.dv), dtype=torch.float32,
+                         device="cuda")
+        ck_off = torch.from_numpy(offs).cuda() if cu is not None else None
+
     def step():
         kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=sN,
                             cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o,
-                            workspace=ws)
+                            workspace=ws, checkpoints=ck, checkpoint_offsets=ck_off,
+                            checkpoint_interval=args.checkpoint_interval)
 
     for _ in range(args.warmup):
         step()
@@ -193,7 +205,8 @@ def main():
     elem = 2 if inp.dtype == "bf16" else 4
     fl, by = prefill_algorithmic(inp.dk, inp.dv, elem)
     tok_heads = inp.total * inp.H
-    state_bytes = (0 if s0 is None else s0.numel() * 4) + (0 if sN is None else sN.numel() * 4)
+    state_bytes = (0 if s0 is None else s0.numel() * 4) + (0 if sN is None else sN.numel() * 4) \
+        + (0 if ck is None else ck.numel() * 4)
     alg_bytes = by * tok_heads + state_bytes
     achieved = alg_bytes / (ms_event * 1e-3) / 1e9
     traffic = read_traffic(name)
@@ -211,6 +224,8 @@ def main():
                    "heads": inp.H, "dk": inp.dk, "dv": inp.dv, "chunk": CHUNK,
                    "initial_state": s0 is not None, "final_state": sN is not None,
                    "workspace_bytes": int(ws.numel()),
+                   "checkpoint_interval": args.checkpoint_interval or None,
+                   "checkpoint_bytes": 0 if ck is None else int(ck.numel() * 4),
                    "cache": "warm: back-to-back calls"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,

@@ -130,6 +130,41 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
                            hipStream_t stream);
 
 /*
+ * kda_prefill_fwd_checkpointed -- kda_prefill_fwd that also writes prefix-cache checkpoints:
+ * the recurrent state at every checkpoint_interval tokens of each sequence.
+ * [K3 note] §9 (KDA keeps one large state per sequence, so checkpoints are affordable only
+ * at sparse, 512-token hash boundaries; a prefix hit restores the state at the boundary and
+ * resumes prefill); [K3 hood] "Serving two incompatible cache types" (checkpoints at
+ * selected hash boundaries, copied read-only into the request's running state).
+ *
+ * All arguments of kda_prefill_fwd keep their meaning, plus:
+ *   checkpoint_interval  tokens between checkpoints, a positive multiple of 64
+ *                        (KDA_ERR_SHAPE otherwise)
+ *   checkpoints          fp32 [n_ckpt, H, dk, dv], 16-byte aligned (NULL: KDA_ERR_NULL).
+ *                        Checkpoint j (0-based) of sequence n is the state after its first
+ *                        (j + 1) * checkpoint_interval tokens, initial_state included, for
+ *                        j < floor(L_n / checkpoint_interval).  It is stored at index
+ *                        first_n + j, where first_n = n * floor(T / checkpoint_interval) for
+ *                        equal-length batches, else checkpoint_offsets[n].
+ *   checkpoint_offsets   device int32 [N + 1]: required (KDA_ERR_NULL) with cu_seqlens, ignored
+ *                        without; the exclusive prefix sum of floor(L_n / checkpoint_interval),
+ *                        which the caller computes from the lengths it packed.  Its contents
+ *                        are not validated.
+ * A checkpoint that falls on a sequence's last token equals that sequence's final state.
+ * Resuming kda_prefill_fwd from checkpoint j (as initial_state) over the remaining tokens
+ * reproduces the original outputs of those tokens exactly (same chunk boundaries).
+ */
+kda_status kda_prefill_fwd_checkpointed(kda_dtype dt, const void* q, const void* k,
+                                        const void* v, const void* beta, const float* z,
+                                        const float* A, float g_min, const float* initial_state,
+                                        float* final_state, const int32_t* cu_seqlens,
+                                        int n_seqs, int64_t T_or_total, int H, int dk, int dv,
+                                        void* o, float* checkpoints,
+                                        const int32_t* checkpoint_offsets,
+                                        int checkpoint_interval, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kda_decode_step -- one recurrent decode step for N sequences x H heads, state in place.
  * [K3 note] §3.2 (the per-token map (x_t, S_{t-1}) -> (y_t, S_t) and its order: decay
  * Sbar = Diag(alpha) S, predict vhat = Sbar^T k, write S = Sbar + beta k (v - vhat)^T,

@@ -88,12 +88,20 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int d
     return kda::split_workspace_bytes(total_tokens, n_seqs, H, dk);
 }
 
-kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const void* v,
-                           const void* beta, const float* z, const float* A, float g_min,
-                           const float* initial_state, float* final_state,
-                           const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
-                           int dk, int dv, void* o, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+namespace {
+
+struct Checkpoints {
+    float* states;           // NULL: none
+    const int32_t* offsets;  // varlen: first checkpoint of each sequence
+    int interval;            // tokens, a positive multiple of 64
+};
+
+kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* v,
+                        const void* beta, const float* z, const float* A, float g_min,
+                        const float* initial_state, float* final_state,
+                        const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
+                        int dk, int dv, void* o, const Checkpoints& ck, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (n_seqs <= 0 || T_or_total < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     const int64_t total = cu_seqlens ? T_or_total : static_cast<int64_t>(n_seqs) * T_or_total;
@@ -117,6 +125,12 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(final_state);
         if (a0 < b0 + bytes && b0 < a0 + bytes) return KDA_ERR_SHAPE;  // partial overlap
     }
+    if (ck.states) {
+        if (ck.interval <= 0 || ck.interval % 64 != 0) return KDA_ERR_SHAPE;
+        if (cu_seqlens && !ck.offsets) return KDA_ERR_NULL;
+        if (!aligned16(ck.states) || (ck.offsets && (reinterpret_cast<uintptr_t>(ck.offsets) & 3u)))
+            return KDA_ERR_ALIGN;
+    }
     if (total == 0 && !final_state) return KDA_OK;  // nothing to compute or write
     const size_t need = kda_prefill_workspace_size(total, n_seqs, H, dk, dv, dt);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
@@ -126,6 +140,12 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     a.s0 = initial_state; a.sN = final_state; a.cu = cu_seqlens; a.n_seqs = n_seqs;
     a.T = cu_seqlens ? 0 : T_or_total; a.H = H; a.o = o; a.npairs = n_seqs * H;
     a.total = total;
+    if (ck.states) {
+        a.ckpt = ck.states;
+        a.ckpt_off = cu_seqlens ? ck.offsets : nullptr;
+        a.ckpt_chunks = ck.interval / 64;
+        a.ckpt_per_seq = cu_seqlens ? 0 : static_cast<int>(T_or_total / ck.interval);
+    }
     const size_t table = ((static_cast<size_t>(n_seqs) + 1) * 4 + 255) / 256 * 256;
     a.chunk_start = static_cast<int32_t*>(workspace);
     a.blocks = static_cast<char*>(workspace) + table;
@@ -136,6 +156,35 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     const int ct = (dk == 128 && 2 * static_cast<int64_t>(a.npairs) > cus) ? 2 : 1;
     return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ct, stream) == hipSuccess ? KDA_OK
                                                                                          : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const void* v,
+                           const void* beta, const float* z, const float* A, float g_min,
+                           const float* initial_state, float* final_state,
+                           const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
+                           int dk, int dv, void* o, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    return prefill_impl(dt, q, k, v, beta, z, A, g_min, initial_state, final_state, cu_seqlens,
+                        n_seqs, T_or_total, H, dk, dv, o, Checkpoints{nullptr, nullptr, 0},
+                        workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_fwd_checkpointed(kda_dtype dt, const void* q, const void* k,
+                                        const void* v, const void* beta, const float* z,
+                                        const float* A, float g_min, const float* initial_state,
+                                        float* final_state, const int32_t* cu_seqlens,
+                                        int n_seqs, int64_t T_or_total, int H, int dk, int dv,
+                                        void* o, float* checkpoints,
+                                        const int32_t* checkpoint_offsets,
+                                        int checkpoint_interval, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    if (!checkpoints) return KDA_ERR_NULL;
+    return prefill_impl(dt, q, k, v, beta, z, A, g_min, initial_state, final_state, cu_seqlens,
+                        n_seqs, T_or_total, H, dk, dv, o,
+                        Checkpoints{checkpoints, checkpoint_offsets, checkpoint_interval},
+                        workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const void* v,

@@ -46,6 +46,10 @@ struct SplitArgs : PrefillArgs {
     int64_t total;           // packed token count
     int32_t* chunk_start;    // [n_seqs + 1] in the workspace (varlen only)
     void* blocks;            // factor blocks in the workspace
+    float* ckpt;             // nullable: states at every ckpt_chunks-th chunk boundary
+    const int32_t* ckpt_off; // [n_seqs + 1] first checkpoint of each sequence (varlen)
+    int ckpt_chunks;         // checkpoint interval in chunks
+    int ckpt_per_seq;        // checkpoints per sequence when ckpt_off is NULL
 };
 
 size_t split_block_bytes(int dk);

@@ -653,6 +653,16 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) Sacc[ct][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // this wave's columns of the state to dst = &S[0][col0 + li] of one (sequence, head)
+    auto store_state = [&](float* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[16 * ct + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] = Sacc[ct][m][r];
+    };
     lds_barrier();
 
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -792,19 +802,16 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
             }
         }
         }  // column tile
+        // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
+        if (args.ckpt && (c + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(c + 1) * kC <= len) {
+            const int j = (c + 1) / args.ckpt_chunks - 1;
+            const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
+            store_state(args.ckpt + ((first + j) * H + h) * DK * dv + col0 + li);
+        }
         lds_barrier();
     }
 
-    if (args.sN) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    args.sN[sbase + 16 * ct + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] =
-                        Sacc[ct][m][r];
-    }
+    if (args.sN) store_state(args.sN + sbase);
 }
 
 // ---- host side --------------------------------------------------------------------------

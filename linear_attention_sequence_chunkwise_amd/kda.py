@@ -20,8 +20,8 @@ KDA_BF16 = 1
 G_MIN = -5.0
 
 # exported symbols, in the order include/kda.h declares them
-SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step",
-           "kda_status_str")
+SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd",
+           "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_status_str")
 
 _lib = None
 
@@ -51,6 +51,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prefill_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32,
                                     i32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_fwd.restype = i32
+    lib.kda_prefill_fwd_checkpointed.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32,
+                                                 i64, i32, i32, i32, vp, vp, vp, i32, vp,
+                                                 ctypes.c_size_t, vp]
+    lib.kda_prefill_fwd_checkpointed.restype = i32
     lib.kda_decode_step.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, vp,
                                     vp]
     lib.kda_decode_step.restype = i32
@@ -121,10 +125,14 @@ def kda_prefill_workspace_size(total_tokens: int, n_seqs: int, H: int, dk: int, 
 
 def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=None,
                     final_state=None, cu_seqlens=None, n_seqs: Optional[int] = None, o=None,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, checkpoints=None, checkpoint_offsets=None,
+                    checkpoint_interval: int = 0):
     """Chunkwise prefill over packed tokens.  q,k,z [total,H,dk]; v [total,H,dv];
     beta [total,H]; A [H,dk]; states [N,H,dk,dv] fp32; cu_seqlens [N+1] int32 or None (then
-    n_seqs equal-length sequences, default 1).  Returns o [total,H,dv]."""
+    n_seqs equal-length sequences, default 1).  Returns o [total,H,dv].
+    With `checkpoints` ([n_ckpt,H,dk,dv] fp32) the call goes to kda_prefill_fwd_checkpointed:
+    the state after every `checkpoint_interval` tokens of each sequence is written there
+    (`checkpoint_offsets` [N+1] int32 is required with cu_seqlens)."""
     lib = load_library()
     total, H, dk = q.shape
     dv = v.shape[2]
@@ -143,7 +151,15 @@ def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=Non
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _dev(q, k, v, beta, z, A, initial_state, final_state, cu_seqlens, o, workspace)
+    _dev(q, k, v, beta, z, A, initial_state, final_state, cu_seqlens, o, workspace, checkpoints,
+         checkpoint_offsets)
+    if checkpoints is not None:
+        _check("kda_prefill_fwd_checkpointed", lib.kda_prefill_fwd_checkpointed(
+            dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
+            _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, T_or_total, H, dk, dv,
+            _ptr(o), _ptr(checkpoints), _ptr(checkpoint_offsets), int(checkpoint_interval),
+            _ptr(workspace), wbytes, _stream(stream)))
+        return o
     _check("kda_prefill_fwd", lib.kda_prefill_fwd(
         dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(initial_state),
         _ptr(final_state), _ptr(cu_seqlens), N, T_or_total, H, dk, dv, _ptr(o), _ptr(workspace),

@@ -75,6 +75,21 @@ def test_prefill_rejects_bad_arguments(lib):
     assert prefill(lib, T=1 << 45, N=1 << 10) == ESHAPE
 
 
+def test_checkpointed_prefill_rejects_bad_arguments(lib):
+    def ck(states=P, offs=None, interval=128, cu=None, T=256, ws=None, wsb=0):
+        return lib.kda_prefill_fwd_checkpointed(BF16, P, P, P, P, P, P, -5.0, None, None, cu, 1, T,
+                                                2, 128, 128, P, states, offs, interval, ws, wsb, None)
+    assert ck(states=None) == ENULL
+    assert ck(interval=0) == ESHAPE
+    assert ck(interval=100) == ESHAPE                  # not a multiple of the 64-token chunk
+    assert ck(interval=-64) == ESHAPE
+    assert ck(cu=P, offs=None) == ENULL                # varlen needs the per-sequence offsets
+    assert ck(states=MIS) == EALIGN
+    assert ck(cu=P, offs=ctypes.c_void_p(0x10002)) == EALIGN
+    assert ck() == EWS                                 # valid so far; no workspace given
+    assert ck(T=0) == OK                               # nothing to compute
+
+
 def test_gate_rejects_bad_arguments(lib):
     def gate(z=P, A=P, g=P, gc=P, T=64, H=2, dk=128, cu=None, N=1, chunk=64, g_min=-5.0):
         return lib.kda_gate(z, A, g, gc, T, H, dk, cu, N, chunk, g_min, None)
