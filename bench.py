@@ -240,6 +240,7 @@ def main():
 
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps)
+        out["spec_decode"] = bench_spec_decode()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
@@ -286,6 +287,55 @@ def bench_decode(n_steps: int, distinct: int = 32, repeats: int = 3):
                          "frac": gbps / HBM_PEAK_GBPS, "traffic": read_traffic(workloads.DECODE),
                          "kernel": "decode_kernel", "algorithmic_bytes_per_launch": byts},
             "inputs": f"{distinct} distinct seeded steps cycled"}
+
+
+def bench_spec_decode(K: int = 4, rounds: int = 32, repeats: int = 3):
+    """Speculative decode rounds over 512 sequences x 32 heads (d = 128, bf16): each round is
+    one kda_decode_verify of K draft tokens from the committed state plus one
+    kda_decode_commit of all K (full acceptance), so a round yields K tokens per sequence.
+    The state is read once by verify and read and written once by commit (3 x 1 GiB per
+    round) instead of 2 x 1 GiB per token.  `rounds` distinct seeded rounds are cycled."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda, workloads
+    d = workloads.decode_inputs(N=512, H=32, dk=128, dv=128, steps=K * 8, dtype="bf16", seed=5,
+                                name="spec_decode_n512_h32_d128_bf16")
+    nk = lambda x: x.reshape(8, K, *x.shape[1:]).transpose(1, 2).contiguous().cuda()  # [8,N,K,..]
+    q, k, v, beta, z = (nk(t) for t in (d.q, d.k, d.v, d.beta, d.z))
+    A = d.A.cuda()
+    s_init = d.S0.cuda()
+    state = s_init.clone()
+    acc = torch.full((d.N,), K, dtype=torch.int32, device="cuda")
+    o = torch.empty((d.N, K, d.H, d.dv), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for r in range(rounds):
+            j = r % 8
+            kda.kda_decode_verify(q[j], k[j], v[j], beta[j], z[j], A, state, o=o)
+            kda.kda_decode_commit(k[j], v[j], beta[j], z[j], A, state, acc)
+
+    run()
+    times = []
+    for _ in range(repeats):
+        state.copy_(s_init)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.median(times)) / rounds
+    pairs = d.N * d.H
+    inp_bytes = K * (3 * 128 * 2 + 2 + 128 * 4)          # q, k, v, beta, z per token
+    byts = pairs * (3 * 128 * 128 * 4 + 2 * inp_bytes - K * 128 * 2 + K * 128 * 2)
+    gbps = byts / t / 1e9
+    return {"workload": "spec_decode_n512_h32_d128_bf16_k%d" % K, "draft_tokens": K,
+            "us_per_round": t * 1e6, "tokens_per_s": d.N * K / t, "hbm_GBps": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "decode_multi_kernel (verify + commit)",
+                         "algorithmic_bytes_per_launch": byts},
+            "inputs": "8 distinct seeded rounds cycled; full acceptance"}
 
 
 if __name__ == "__main__":

@@ -61,6 +61,8 @@ typedef enum kda_dtype {
 
 /* Largest chunk length accepted by kda_gate. */
 #define KDA_GATE_MAX_CHUNK 1024
+/* most draft tokens kda_decode_verify / kda_decode_commit take per call */
+#define KDA_DECODE_MAX_DRAFT 16
 
 /*
  * kda_gate -- lower-bounded decay gate and chunk-local cumulative log-decay.
@@ -180,6 +182,39 @@ kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const voi
                            const void* beta, const float* z, const float* A, float g_min,
                            float* state, int N, int H, int dk, int dv, void* o,
                            hipStream_t stream);
+
+/*
+ * kda_decode_verify -- outputs of K draft tokens per sequence from the committed state,
+ * which is only read.  [K3 hood] "Serving two incompatible cache types" (rejected draft
+ * tokens must not advance the recurrent state; the small projected inputs are kept and the
+ * accepted ones replayed on chip); [K3 note] §3.2 (each token's output is read after its
+ * own write).  o[n, t] equals what t + 1 consecutive kda_decode_step calls on draft tokens
+ * 0..t would return for token t; the state is read once for all K tokens.
+ *
+ *   q, k, z        [N, K, H, dk];  v [N, K, H, dv];  beta [N, K, H];  A [H, dk] fp32
+ *   state          fp32 [N, H, dk, dv], read only
+ *   K              1 .. KDA_DECODE_MAX_DRAFT draft tokens per sequence (KDA_ERR_SHAPE else)
+ *   o              [N, K, H, dv] output of type dt
+ *   dk, dv         64 or 128 each, dk == dv
+ */
+kda_status kda_decode_verify(kda_dtype dt, const void* q, const void* k, const void* v,
+                             const void* beta, const float* z, const float* A, float g_min,
+                             const float* state, int N, int K, int H, int dk, int dv, void* o,
+                             hipStream_t stream);
+
+/*
+ * kda_decode_commit -- advance each sequence's state in place by its accepted draft tokens:
+ * replays the first accepted[n] of the K tokens given to kda_decode_verify (same k, v, beta,
+ * z; q is not needed), reading and writing the state once.  Same sources as above.
+ *
+ *   accepted       device int32 [N]; values are clamped to [0, K]; 0 leaves the state as is
+ *   other arguments as for kda_decode_verify; state fp32 [N, H, dk, dv] read and written
+ * The result equals accepted[n] consecutive kda_decode_step calls.
+ */
+kda_status kda_decode_commit(kda_dtype dt, const void* k, const void* v, const void* beta,
+                             const float* z, const float* A, float g_min, float* state, int N,
+                             int K, int H, int dk, int dv, const int32_t* accepted,
+                             hipStream_t stream);
 
 /* kda_status_str -- a static, human-readable name for a status code. */
 const char* kda_status_str(kda_status status);

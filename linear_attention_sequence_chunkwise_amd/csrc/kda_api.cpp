@@ -207,4 +207,46 @@ kda_status kda_decode_step(kda_dtype dt, const void* q, const void* k, const voi
     return kda::launch_decode(a, dk, dt == KDA_BF16, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_decode_verify(kda_dtype dt, const void* q, const void* k, const void* v,
+                             const void* beta, const float* z, const float* A, float g_min,
+                             const float* state, int N, int K, int H, int dk, int dv, void* o,
+                             hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || K < 1 || K > KDA_DECODE_MAX_DRAFT) return KDA_ERR_SHAPE;
+    if (N > 0 && (!q || !k || !v || !beta || !z || !A || !state || !o)) return KDA_ERR_NULL;
+    if (!supported_d(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(g_min) || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(N) * H > int64_t(0x7fffffff)) return KDA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||
+        !aligned16(z) || !aligned16(A) || !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    if (N == 0) return KDA_OK;
+    kda::DecodeMultiArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.z = z; a.A = A; a.g_min = g_min;
+    a.state_in = state; a.N = N; a.K = K; a.H = H; a.o = o;
+    return kda::launch_decode_multi(a, dk, dt == KDA_BF16, false, stream) == hipSuccess ? KDA_OK
+                                                                                          : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_commit(kda_dtype dt, const void* k, const void* v, const void* beta,
+                             const float* z, const float* A, float g_min, float* state, int N,
+                             int K, int H, int dk, int dv, const int32_t* accepted,
+                             hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || K < 1 || K > KDA_DECODE_MAX_DRAFT) return KDA_ERR_SHAPE;
+    if (N > 0 && (!k || !v || !beta || !z || !A || !state || !accepted)) return KDA_ERR_NULL;
+    if (!supported_d(dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(g_min) || !(g_min < 0.f)) return KDA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(N) * H > int64_t(0x7fffffff)) return KDA_ERR_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) || !aligned16(z) ||
+        !aligned16(A) || !aligned16(state) || (reinterpret_cast<uintptr_t>(accepted) & 3u))
+        return KDA_ERR_ALIGN;
+    if (N == 0) return KDA_OK;
+    kda::DecodeMultiArgs a{};
+    a.k = k; a.v = v; a.beta = beta; a.z = z; a.A = A; a.g_min = g_min;
+    a.state = state; a.accepted = accepted; a.N = N; a.K = K; a.H = H;
+    return kda::launch_decode_multi(a, dk, dt == KDA_BF16, true, stream) == hipSuccess ? KDA_OK
+                                                                                         : KDA_ERR_HIP;
+}
+
 }  // extern "C"

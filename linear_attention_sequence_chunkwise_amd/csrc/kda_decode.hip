@@ -113,6 +113,149 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeArgs args) {
     }
 }
 
+// ---- several tokens per call: speculative verify and commit ----------------------------
+// [K3 hood] "Serving two incompatible cache types": rejected draft tokens must not advance
+// the recurrent state, and saving a full state per draft position would multiply memory
+// traffic; instead the (small) projected inputs are kept and the accepted tokens replayed
+// on chip.  verify: from the committed state, the outputs of draft tokens 0..K-1 (each after
+// its own write, [K3 note] §3.2), the state only read.  commit: the state advanced in place
+// by the first accepted[n] of the same tokens.  Each reads the state once per call (and
+// commit writes it once) instead of once per token.  Layout and thread tiling as in the
+// single-token kernel; the K tokens' inputs are staged in LDS first.
+template <int D, int NT, typename TIn, bool COMMIT>
+__global__ void __launch_bounds__(NT) decode_multi_kernel(DecodeMultiArgs args) {
+    constexpr int COLG = D / 4;
+    constexpr int ROWG = NT / COLG;
+    constexpr int RPT = D / ROWG;
+    constexpr int NWV = NT / 64;
+    constexpr int KM = kDecodeMaxDraft;
+    static_assert(NT % COLG == 0 && D % ROWG == 0 && COLG <= 64 && D <= NT && NWV >= 1, "thread tiling");
+
+    __shared__ float s_alpha[KM][D], s_k[KM][D], s_q[COMMIT ? 1 : KM][D], s_v[KM][D];
+    __shared__ float s_beta[KM], s_kq[KM], s_u[D];
+    __shared__ float s_red[NWV][2][D];
+
+    const int tid = threadIdx.x;
+    const int pair = blockIdx.x;
+    const int H = args.H, K = args.K;
+    const int n = pair / H, h = pair - n * H;
+    int ntok = K;
+    if constexpr (COMMIT) {
+        const int acc = args.accepted[n];
+        ntok = acc < 0 ? 0 : acc > K ? K : acc;
+        if (ntok == 0) return;  // nothing accepted: the state stays as it is
+    }
+
+    // stage the inputs of the ntok tokens: gate, k, q, v per channel; beta per token
+    for (int idx = tid; idx < ntok * D; idx += NT) {
+        const int t = idx / D, c = idx - t * D;
+        const size_t vec = ((static_cast<size_t>(n) * K + t) * H + h) * D + c;
+        const float a = -expf(args.A[h * D + c]) * kLog2e;
+        const float sg = fast_rcp(1.f + fast_exp2(a * args.z[vec]));
+        s_alpha[t][c] = fast_exp2(args.g_min * kLog2e * sg);
+        s_k[t][c] = Elem<TIn>::load1(static_cast<const TIn*>(args.k) + vec);
+        if constexpr (!COMMIT) s_q[t][c] = Elem<TIn>::load1(static_cast<const TIn*>(args.q) + vec);
+        s_v[t][c] = Elem<TIn>::load1(static_cast<const TIn*>(args.v) + vec);
+    }
+    for (int t = tid; t < ntok; t += NT)
+        s_beta[t] = Elem<TIn>::load1(static_cast<const TIn*>(args.beta) + (static_cast<size_t>(n) * K + t) * H + h);
+
+    const int cg = tid % COLG, rg = tid / COLG;
+    const size_t sofs = static_cast<size_t>(pair) * D * D;
+    const f32x4_t* __restrict__ sin = reinterpret_cast<const f32x4_t*>((COMMIT ? args.state : args.state_in) + sofs);
+    float4 S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const f32x4_t t4 = __builtin_nontemporal_load(&sin[(rg + ROWG * i) * COLG + cg]);
+        S[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+    }
+    __syncthreads();
+    if constexpr (!COMMIT) {  // k . q of every token (one wave per token)
+        const int wv = tid >> 6, ln = tid & 63;
+        for (int t = wv; t < ntok; t += NWV) {
+            float x = 0.f;
+            for (int c = ln; c < D; c += 64) x += s_k[t][c] * s_q[t][c];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            if (ln == 0) s_kq[t] = x;
+        }
+    }
+
+    const int wv = tid >> 6;
+    for (int t = 0; t < ntok; ++t) {
+        float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + ROWG * i;
+            const float al = s_alpha[t][r], kr = s_k[t][r];
+            S[i].x *= al; S[i].y *= al; S[i].z *= al; S[i].w *= al;  // Sbar
+            pk.x += S[i].x * kr; pk.y += S[i].y * kr; pk.z += S[i].z * kr; pk.w += S[i].w * kr;
+            if constexpr (!COMMIT) {
+                const float qr = s_q[t][r];
+                pq.x += S[i].x * qr; pq.y += S[i].y * qr; pq.z += S[i].z * qr; pq.w += S[i].w * qr;
+            }
+        }
+#pragma unroll
+        for (int off = COLG; off < 64; off <<= 1) {
+            pk.x += __shfl_xor(pk.x, off); pk.y += __shfl_xor(pk.y, off);
+            pk.z += __shfl_xor(pk.z, off); pk.w += __shfl_xor(pk.w, off);
+            if constexpr (!COMMIT) {
+                pq.x += __shfl_xor(pq.x, off); pq.y += __shfl_xor(pq.y, off);
+                pq.z += __shfl_xor(pq.z, off); pq.w += __shfl_xor(pq.w, off);
+            }
+        }
+        if ((tid & 63) < COLG) {
+            *reinterpret_cast<float4*>(&s_red[wv][0][4 * cg]) = pk;
+            if constexpr (!COMMIT) *reinterpret_cast<float4*>(&s_red[wv][1][4 * cg]) = pq;
+        }
+        __syncthreads();
+        if (tid < D) {
+            float vk = 0.f, vq = 0.f;
+#pragma unroll
+            for (int x = 0; x < NWV; ++x) {
+                vk += s_red[x][0][tid];
+                if constexpr (!COMMIT) vq += s_red[x][1][tid];
+            }
+            const float u = s_beta[t] * (s_v[t][tid] - vk);
+            s_u[tid] = u;
+            if constexpr (!COMMIT)
+                Elem<TIn>::store1(static_cast<TIn*>(args.o) + ((static_cast<size_t>(n) * K + t) * H + h) * D + tid,
+                                  vq + s_kq[t] * u);
+        }
+        __syncthreads();
+        const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kr = s_k[t][rg + ROWG * i];
+            S[i].x += kr * u4.x; S[i].y += kr * u4.y; S[i].z += kr * u4.z; S[i].w += kr * u4.w;
+        }
+    }
+    if constexpr (COMMIT) {
+        f32x4_t* __restrict__ st = reinterpret_cast<f32x4_t*>(args.state + sofs);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            __builtin_nontemporal_store(f32x4_t{S[i].x, S[i].y, S[i].z, S[i].w}, &st[(rg + ROWG * i) * COLG + cg]);
+    }
+}
+
+template <int D, int NT, typename TIn>
+static void launch_multi_t(const DecodeMultiArgs& a, bool commit, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H));
+    if (commit) hipLaunchKernelGGL((decode_multi_kernel<D, NT, TIn, true>), grid, dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((decode_multi_kernel<D, NT, TIn, false>), grid, dim3(NT), 0, stream, a);
+}
+
+hipError_t launch_decode_multi(const DecodeMultiArgs& a, int d, bool bf16, bool commit, hipStream_t stream) {
+    if (d == 128) {
+        if (bf16) launch_multi_t<128, 1024, bf16_t>(a, commit, stream);
+        else launch_multi_t<128, 1024, float>(a, commit, stream);
+    } else {
+        if (bf16) launch_multi_t<64, 512, bf16_t>(a, commit, stream);
+        else launch_multi_t<64, 512, float>(a, commit, stream);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H));
     if (d == 128) {

@@ -71,7 +71,26 @@ struct DecodeArgs {
     void* o;
 };
 
+// Several consecutive tokens per sequence with the state held on chip: verify (outputs of
+// every draft token, state read only) or commit (state advanced by accepted[n] tokens).
+struct DecodeMultiArgs {
+    const void* q;          // [N, K, H, dk] (verify only)
+    const void* k;
+    const void* v;          // [N, K, H, dv]
+    const void* beta;       // [N, K, H]
+    const float* z;         // [N, K, H, dk]
+    const float* A;
+    float g_min;
+    const float* state_in;  // verify
+    float* state;           // commit (in place)
+    const int32_t* accepted;  // commit: tokens to replay per sequence, clamped to [0, K]
+    int N, K, H;
+    void* o;                // verify: [N, K, H, dv]
+};
+constexpr int kDecodeMaxDraft = 16;
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeMultiArgs& a, int d, bool bf16, bool commit, hipStream_t stream);
 
 }  // namespace kda

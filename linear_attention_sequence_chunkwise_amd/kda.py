@@ -21,7 +21,9 @@ G_MIN = -5.0
 
 # exported symbols, in the order include/kda.h declares them
 SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd",
-           "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_status_str")
+           "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_decode_verify",
+           "kda_decode_commit", "kda_status_str")
+MAX_DRAFT = 16
 
 _lib = None
 
@@ -58,6 +60,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, vp,
                                     vp]
     lib.kda_decode_step.restype = i32
+    lib.kda_decode_verify.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32,
+                                      i32, vp, vp]
+    lib.kda_decode_verify.restype = i32
+    lib.kda_decode_commit.argtypes = [i32, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, i32,
+                                      vp, vp]
+    lib.kda_decode_commit.restype = i32
     _lib = lib
     return lib
 
@@ -180,3 +188,32 @@ def kda_decode_step(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, st
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
         _ptr(state), N, H, dk, dv, _ptr(o), _stream(stream)))
     return o
+
+
+def kda_decode_verify(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, stream=None):
+    """Outputs of K draft tokens per sequence from the committed state (read only);
+    q,k,z [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]; state [N,H,dk,dv] fp32.
+    Returns o [N,K,H,dv]."""
+    lib = load_library()
+    N, K, H, dk = q.shape
+    dv = v.shape[3]
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, beta, z, A, state, o)
+    _check("kda_decode_verify", lib.kda_decode_verify(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
+        _ptr(state), N, K, H, dk, dv, _ptr(o), _stream(stream)))
+    return o
+
+
+def kda_decode_commit(k, v, beta, z, A, state, accepted, g_min: float = G_MIN, stream=None):
+    """Advance state [N,H,dk,dv] in place by the first accepted[n] (device int32 [N]) of the
+    K draft tokens k,z [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]."""
+    lib = load_library()
+    N, K, H, dk = k.shape
+    dv = v.shape[3]
+    _dev(k, v, beta, z, A, state, accepted)
+    _check("kda_decode_commit", lib.kda_decode_commit(
+        _dtype_code(k), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(state), N, K,
+        H, dk, dv, _ptr(accepted), _stream(stream)))
+    return state

@@ -120,6 +120,22 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(N=0, q=None, state=None, o=None) == OK
 
 
+def test_verify_and_commit_reject_bad_arguments(lib):
+    def ver(q=P, state=P, N=4, K=4, dk=128, dv=128, o=P):
+        return lib.kda_decode_verify(BF16, q, P, P, P, P, P, -5.0, state, N, K, 2, dk, dv, o, None)
+    def com(k=P, state=P, acc=P, N=4, K=4, dk=128, dv=128):
+        return lib.kda_decode_commit(BF16, k, P, P, P, P, -5.0, state, N, K, 2, dk, dv, acc, None)
+    assert ver(q=None) == ENULL and ver(state=None) == ENULL and ver(o=None) == ENULL
+    assert ver(K=0) == ESHAPE and ver(K=17) == ESHAPE and ver(N=-1) == ESHAPE
+    assert ver(dk=96, dv=96) == EUNSUP
+    assert ver(state=MIS) == EALIGN
+    assert ver(N=0) == OK
+    assert com(k=None) == ENULL and com(acc=None) == ENULL
+    assert com(K=0) == ESHAPE and com(K=17) == ESHAPE
+    assert com(acc=ctypes.c_void_p(0x10002)) == EALIGN
+    assert com(N=0) == OK
+
+
 def test_workspace_size_is_aligned(lib):
     for args in [(4096, 1, 16, 128, 128, BF16), (293000, 64, 32, 128, 128, BF16), (256, 1, 2, 64, 64, F32)]:
         assert lib.kda_prefill_workspace_size(*args) % 256 == 0
