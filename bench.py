@@ -326,8 +326,10 @@ def bench_spec_decode(K: int = 4, rounds: int = 32, repeats: int = 3):
         times.append(e0.elapsed_time(e1) * 1e-3)
     t = float(np.median(times)) / rounds
     pairs = d.N * d.H
-    inp_bytes = K * (3 * 128 * 2 + 2 + 128 * 4)          # q, k, v, beta, z per token
-    byts = pairs * (3 * 128 * 128 * 4 + 2 * inp_bytes - K * 128 * 2 + K * 128 * 2)
+    state = 128 * 128 * 4
+    verify = state + K * (3 * 128 * 2 + 2 + 128 * 4) + K * 128 * 2   # q,k,v,beta,z in; o out
+    commit = 2 * state + K * (2 * 128 * 2 + 2 + 128 * 4)              # k,v,beta,z in
+    byts = pairs * (verify + commit)
     gbps = byts / t / 1e9
     return {"workload": "spec_decode_n512_h32_d128_bf16_k%d" % K, "draft_tokens": K,
             "us_per_round": t * 1e6, "tokens_per_s": d.N * K / t, "hbm_GBps": gbps,
