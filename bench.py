@@ -241,6 +241,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps)
         out["spec_decode"] = bench_spec_decode()
+        out["output_gate"] = bench_output_gate()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
@@ -338,6 +339,36 @@ def bench_spec_decode(K: int = 4, rounds: int = 32, repeats: int = 3):
                          "kernel": "decode_multi_kernel (verify + commit)",
                          "algorithmic_bytes_per_launch": byts},
             "inputs": "8 distinct seeded rounds cycled; full acceptance"}
+
+
+def bench_output_gate(repeats: int = 10):
+    """Fused epilogue y = Sigmoid(gate) * RMSNorm(o) over the readout of the batched prefill
+    workload (4 x 32768 tokens x 32 heads, d_v = 128, bf16): 3 x 1.07 GB moved."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda
+    rows, dv = 4 * 32768 * 32, 128
+    g = torch.Generator(device="cuda").manual_seed(6)
+    o = (torch.randn(rows, dv, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    gate = torch.randn(rows, dv, device="cuda", generator=g).to(torch.bfloat16)
+    w = torch.ones(dv, device="cuda")
+    y = torch.empty_like(o)
+    kda.kda_output_gate(o, gate, w, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(repeats):
+        kda.kda_output_gate(o, gate, w, y=y)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / repeats
+    byts = 3 * rows * dv * 2 + dv * 4
+    gbps = byts / t / 1e9
+    del o, gate, y
+    return {"workload": "output_gate_rows4194304_dv128_bf16", "us_per_call": t * 1e6,
+            "hbm_GBps": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "output_gate_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
 if __name__ == "__main__":

@@ -216,6 +216,21 @@ kda_status kda_decode_commit(kda_dtype dt, const void* k, const void* v, const v
                              int K, int H, int dk, int dv, const int32_t* accepted,
                              hipStream_t stream);
 
+/*
+ * kda_output_gate -- fused output epilogue y = Sigmoid(gate) * RMSNorm(o), per row.
+ * [K3 note] §3.2 (the K3 output path W_o[Sigmoid(W_g x_t) (.) RMSNorm(o~_t)]; the projections
+ * need trained weights, so this entry takes the readout o~ and the gate logits W_g x_t).
+ * RMSNorm(o) = o / sqrt(mean(o^2) + eps) * weight, over the d_v channels of one row.
+ *
+ *   dt        element type of o, gate and y
+ *   o, gate   [rows, dv] (a row is one token of one head, e.g. rows = tokens * H)
+ *   weight    fp32 [dv];  eps finite and >= 0
+ *   y         [rows, dv] output of type dt; may be o itself (in place)
+ *   dv        64 or 128
+ */
+kda_status kda_output_gate(kda_dtype dt, const void* o, const void* gate, const float* weight,
+                           float eps, int64_t rows, int dv, void* y, hipStream_t stream);
+
 /* kda_status_str -- a static, human-readable name for a status code. */
 const char* kda_status_str(kda_status status);
 

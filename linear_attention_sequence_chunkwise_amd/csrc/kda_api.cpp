@@ -249,4 +249,19 @@ kda_status kda_decode_commit(kda_dtype dt, const void* k, const void* v, const v
                                                                                          : KDA_ERR_HIP;
 }
 
+kda_status kda_output_gate(kda_dtype dt, const void* o, const void* gate, const float* weight,
+                           float eps, int64_t rows, int dv, void* y, hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (rows < 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dv != 64 && dv != 128) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(eps) || eps < 0.f) return KDA_ERR_UNSUPPORTED;
+    if (!weight || (rows > 0 && (!o || !gate || !y))) return KDA_ERR_NULL;
+    if (rows > kMaxElems / dv) return KDA_ERR_SHAPE;
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(weight) || !aligned16(y)) return KDA_ERR_ALIGN;
+    if (rows == 0) return KDA_OK;
+    kda::OutputGateArgs a{};
+    a.o = o; a.gate = gate; a.w = weight; a.eps = eps; a.rows = rows; a.y = y;
+    return kda::launch_output_gate(a, dv, dt == KDA_BF16, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

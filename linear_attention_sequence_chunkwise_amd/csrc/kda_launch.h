@@ -89,7 +89,17 @@ struct DecodeMultiArgs {
 };
 constexpr int kDecodeMaxDraft = 16;
 
+struct OutputGateArgs {
+    const void* o;      // [rows, dv]
+    const void* gate;   // [rows, dv] gate logits
+    const float* w;     // [dv] RMSNorm weight
+    float eps;
+    int64_t rows;
+    void* y;            // [rows, dv]
+};
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+hipError_t launch_output_gate(const OutputGateArgs& a, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a, int d, bool bf16, bool commit, hipStream_t stream);
 

@@ -22,7 +22,7 @@ G_MIN = -5.0
 # exported symbols, in the order include/kda.h declares them
 SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd",
            "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_decode_verify",
-           "kda_decode_commit", "kda_status_str")
+           "kda_decode_commit", "kda_output_gate", "kda_status_str")
 MAX_DRAFT = 16
 
 _lib = None
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_commit.argtypes = [i32, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, i32,
                                       vp, vp]
     lib.kda_decode_commit.restype = i32
+    lib.kda_output_gate.argtypes = [i32, vp, vp, vp, f32, i64, i32, vp, vp]
+    lib.kda_output_gate.restype = i32
     _lib = lib
     return lib
 
@@ -217,3 +219,18 @@ def kda_decode_commit(k, v, beta, z, A, state, accepted, g_min: float = G_MIN, s
         _dtype_code(k), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(state), N, K,
         H, dk, dv, _ptr(accepted), _stream(stream)))
     return state
+
+
+def kda_output_gate(o, gate, weight, eps: float = 1e-6, y=None, stream=None):
+    """y = Sigmoid(gate) * o / sqrt(mean(o^2) + eps) * weight over the last axis (dv);
+    o, gate [..., dv] of one dtype; weight [dv] fp32.  Returns y (new, or the given tensor)."""
+    lib = load_library()
+    dv = o.shape[-1]
+    rows = o.numel() // dv if dv else 0
+    if y is None:
+        y = torch.empty_like(o)
+    _dev(o, gate, weight, y)
+    _check("kda_output_gate", lib.kda_output_gate(
+        _dtype_code(o), _ptr(o), _ptr(gate), _ptr(weight), float(eps), rows, dv, _ptr(y),
+        _stream(stream)))
+    return y

@@ -69,6 +69,9 @@ class Oracle:
                                            ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, _dp,
                                            _dp, ctypes.c_int]
         lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_output_gate.argtypes = [_fp, _fp, _fp, ctypes.c_double, ctypes.c_int64,
+                                               ctypes.c_int, _dp]
+        lib.kda_oracle_output_gate.restype = None
         lib.kda_oracle_decode_step.argtypes = [_fp, _fp, _fp, _fp, _fp, _fp, ctypes.c_double,
                                                _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, _ip, ctypes.c_int, _dp,
@@ -180,6 +183,17 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"kda_oracle_decode_step failed: {rc}")
         return o
+
+    def output_gate(self, o, gate, w, eps: float = 1e-6):
+        """y = Sigmoid(gate) * o / sqrt(mean(o^2) + eps) * w per row of the last axis (fp64)."""
+        o, gate, w = _f32(o), _f32(gate), _f32(w)
+        dv = o.shape[-1]
+        rows = o.size // dv
+        assert gate.shape == o.shape and w.shape == (dv,)
+        y = np.empty(o.shape, dtype=np.float64)
+        self.lib.kda_oracle_output_gate(_ptr(o, _fp), _ptr(gate, _fp), _ptr(w, _fp), float(eps),
+                                        rows, dv, _ptr(y, _dp))
+        return y
 
 
 _default: Optional[Oracle] = None

@@ -341,3 +341,26 @@ int kda_oracle_decode_step(const float *q, const float *k, const float *v, const
     }
     return failed ? KDA_ORACLE_ENOMEM : KDA_ORACLE_OK;
 }
+
+/*
+ * Output epilogue, per row (one token of one head): y = Sigmoid(gate) * RMSNorm(o) with
+ * RMSNorm(o) = o / sqrt(mean(o^2) + eps) * w.  [K3 note] §3.2: the K3 output path is
+ * W_o[Sigmoid(W_g x_t) (.) RMSNorm(o~_t)]; the projections need trained weights, so the gate
+ * logits (W_g x_t) arrive as an input.  The pages do not spell out RMSNorm; the plain
+ * reading taken here: root mean square over the head's d_v readout channels, a per-channel
+ * weight w, and an additive eps inside the root.
+ */
+void kda_oracle_output_gate(const float *o, const float *gate, const float *w, double eps,
+                            int64_t rows, int dv, double *y)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *orow = o + r * dv, *grow = gate + r * dv;
+        double ss = 0.0;
+        for (int c = 0; c < dv; ++c) ss += (double)orow[c] * (double)orow[c];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        for (int c = 0; c < dv; ++c) {
+            const double sg = 1.0 / (1.0 + exp(-(double)grow[c]));
+            y[r * dv + c] = (double)orow[c] * inv * (double)w[c] * sg;
+        }
+    }
+}

@@ -136,6 +136,18 @@ def test_verify_and_commit_reject_bad_arguments(lib):
     assert com(N=0) == OK
 
 
+def test_output_gate_rejects_bad_arguments(lib):
+    def og(dt=BF16, o=P, gate=P, w=P, eps=1e-6, rows=16, dv=128, y=P):
+        return lib.kda_output_gate(dt, o, gate, w, eps, rows, dv, y, None)
+    assert og(o=None) == ENULL and og(gate=None) == ENULL and og(y=None) == ENULL
+    assert og(w=None) == ENULL
+    assert og(rows=-1) == ESHAPE
+    assert og(dv=96) == EUNSUP and og(dt=5) == EUNSUP
+    assert og(eps=-1.0) == EUNSUP and og(eps=float("inf")) == EUNSUP
+    assert og(o=MIS) == EALIGN
+    assert og(rows=0, o=None, gate=None, y=None) == OK
+
+
 def test_workspace_size_is_aligned(lib):
     for args in [(4096, 1, 16, 128, 128, BF16), (293000, 64, 32, 128, 128, BF16), (256, 1, 2, 64, 64, F32)]:
         assert lib.kda_prefill_workspace_size(*args) % 256 == 0

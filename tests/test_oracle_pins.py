@@ -3,6 +3,8 @@ from __future__ import annotations
 
 import math
 
+import os
+
 import numpy as np
 import pytest
 
@@ -100,3 +102,47 @@ def test_chunk_affine_map_matches_explicit_product():
         bb = Mt @ bb + beta[t] * np.outer(k[t], v[t])
     assert np.max(np.abs(M - P)) < 1e-12
     assert np.max(np.abs(b - bb)) < 1e-12
+
+
+# ---- output epilogue: y = Sigmoid(gate) * RMSNorm(o) ------------------------------------
+
+def _golden_rows(name):
+    rows = []
+    for line in open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)):
+        if line.strip() and not line.startswith("#"):
+            rows.append([float(x) for x in line.split()])
+    return np.array(rows)
+
+
+def test_output_gate_worked_example(oracle_lib):
+    g = _golden_rows("output_gate_worked_example.txt")
+    o, gate, w, y_exp = g[:, 0], g[:, 1], g[:, 2], g[:, 3]
+    y = oracle_lib.output_gate(o[None].astype(np.float32), gate[None].astype(np.float32),
+                               w.astype(np.float32), eps=0.0)
+    # ln 3 is rounded to fp32 on the way in; Sigmoid moves by < 1e-7 relative
+    assert np.allclose(y[0], y_exp, rtol=1e-6, atol=0)
+
+
+def test_output_gate_closed_forms(oracle_lib):
+    dv = 8
+    w = np.linspace(0.5, 2.0, dv).astype(np.float32)
+    # a constant row c: rms = |c|, so y = sign(c) * c^2/sqrt(c^2 + eps) / |c| * w * Sigmoid(g)
+    for c in (0.25, -3.0):
+        o = np.full((1, dv), c, np.float32)
+        gate = np.zeros((1, dv), np.float32)
+        y = oracle_lib.output_gate(o, gate, w, eps=1e-6)
+        assert np.allclose(y[0], c / np.sqrt(c * c + 1e-6) * w * 0.5, rtol=1e-12)
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((3, dv)).astype(np.float32)
+    # saturated gates: Sigmoid -> 0 and -> 1
+    y_off = oracle_lib.output_gate(o, np.full_like(o, -60.0), w, eps=1e-6)
+    y_on = oracle_lib.output_gate(o, np.full_like(o, 60.0), w, eps=1e-6)
+    assert np.abs(y_off).max() < 1e-25
+    rms = np.sqrt((o.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    assert np.allclose(y_on, o / rms * w, rtol=1e-12)
+    # eps = 0: invariant to rescaling the readout, and each row has unit RMS before w
+    y1 = oracle_lib.output_gate(o, np.full_like(o, 60.0), np.ones(dv, np.float32), eps=0.0)
+    y2 = oracle_lib.output_gate((o * 8.0).astype(np.float32), np.full_like(o, 60.0),
+                                np.ones(dv, np.float32), eps=0.0)
+    assert np.allclose(y1, y2, rtol=1e-12)
+    assert np.allclose((y1 ** 2).mean(axis=1), 1.0, rtol=1e-12)
