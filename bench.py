@@ -242,6 +242,7 @@ def main():
         out["decode"] = bench_decode(args.decode_steps)
         out["spec_decode"] = bench_spec_decode()
         out["output_gate"] = bench_output_gate()
+        out["short_conv"] = bench_short_conv()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
@@ -369,6 +370,40 @@ def bench_output_gate(repeats: int = 10):
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                          "kernel": "output_gate_kernel", "algorithmic_bytes_per_launch": byts}}
+
+
+def bench_short_conv(repeats: int = 10):
+    """Input prologue y = L2Norm(Swish(ShortConv(x))) (width 4, per-head L2Norm) over the
+    q branch of the batched prefill workload: 4 x 32768 tokens x 32 heads x 128 channels,
+    bf16, with caches in and out: 2 x 1.07 GB moved."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda
+    N, T, C, width = 4, 32768, 32 * 128, 4
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(N * T, C, device="cuda", generator=g).to(torch.bfloat16)
+    w = torch.randn(C, width, device="cuda", generator=g) * 0.5
+    cache = torch.zeros(N, C, width - 1, device="cuda")
+    cache_out = torch.empty_like(cache)
+    y = torch.empty_like(x)
+    run = lambda: kda.kda_short_conv(x, w, cache_in=cache, cache_out=cache_out, n_seqs=N,
+                                     l2_group=128, y=y)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(repeats):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / repeats
+    byts = 2 * N * T * C * 2 + C * width * 4 + 2 * cache.numel() * 4
+    gbps = byts / t / 1e9
+    del x, y
+    return {"workload": "short_conv_b4_t32768_c4096_w4_bf16", "us_per_call": t * 1e6,
+            "hbm_GBps": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "short_conv_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
 if __name__ == "__main__":

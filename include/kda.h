@@ -61,6 +61,8 @@ typedef enum kda_dtype {
 
 /* Largest chunk length accepted by kda_gate. */
 #define KDA_GATE_MAX_CHUNK 1024
+/* widest ShortConv kda_short_conv supports */
+#define KDA_SHORT_CONV_MAX_WIDTH 4
 /* most draft tokens kda_decode_verify / kda_decode_commit take per call */
 #define KDA_DECODE_MAX_DRAFT 16
 
@@ -230,6 +232,32 @@ kda_status kda_decode_commit(kda_dtype dt, const void* k, const void* v, const v
  */
 kda_status kda_output_gate(kda_dtype dt, const void* o, const void* gate, const float* weight,
                            float eps, int64_t rows, int dv, void* y, hipStream_t stream);
+
+/*
+ * kda_short_conv -- KDA input prologue: y = Swish(ShortConv(x)), then L2Norm per head when
+ * l2_group > 0 (the q and k branches; 0 for v).  [K3 note] §3.2 (q, k = L2Norm(Swish(
+ * ShortConv(W x))), v = Swish(ShortConv(W_v x)); during decoding ShortConv also reads and
+ * updates the layer's short-convolution cache C^conv).  The projections need trained
+ * weights, so x is the projected input.  ShortConv is a causal depthwise convolution over
+ * the tokens of each sequence: y_t[c] = sum_i weight[c][i] * x_{t-width+1+i}[c] (the last tap
+ * on the current token); Swish(u) = u Sigmoid(u); L2Norm divides each group of l2_group
+ * channels by sqrt(sum u^2 + 1e-6).  A decode step is a call with one token per sequence.
+ *
+ *   dt          element type of x and y
+ *   x           [total, C] packed tokens (C = heads x head dim, a multiple of 8)
+ *   weight      fp32 [C, width], width 1 .. KDA_SHORT_CONV_MAX_WIDTH
+ *   cache_in    fp32 [N, C, width-1] or NULL (zeros): the width-1 inputs that precede each
+ *               sequence, oldest first
+ *   cache_out   fp32 [N, C, width-1] or NULL: receives the last width-1 inputs of each
+ *               sequence (reaching into cache_in for shorter sequences); may be cache_in
+ *   cu_seqlens  device int32 [N + 1], or NULL for N sequences of T_or_total tokens
+ *   l2_group    0, 64 or 128 (C a multiple of it)
+ *   y           [total, C] of type dt; must not be x
+ */
+kda_status kda_short_conv(kda_dtype dt, const void* x, const float* weight, int width,
+                          const float* cache_in, float* cache_out, const int32_t* cu_seqlens,
+                          int n_seqs, int64_t T_or_total, int C, int l2_group, void* y,
+                          hipStream_t stream);
 
 /* kda_status_str -- a static, human-readable name for a status code. */
 const char* kda_status_str(kda_status status);

@@ -264,4 +264,32 @@ kda_status kda_output_gate(kda_dtype dt, const void* o, const void* gate, const 
     return kda::launch_output_gate(a, dv, dt == KDA_BF16, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_short_conv(kda_dtype dt, const void* x, const float* weight, int width,
+                          const float* cache_in, float* cache_out, const int32_t* cu_seqlens,
+                          int n_seqs, int64_t T_or_total, int C, int l2_group, void* y,
+                          hipStream_t stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (n_seqs <= 0 || T_or_total < 0 || C <= 0) return KDA_ERR_SHAPE;
+    if (width < 1 || width > KDA_SHORT_CONV_MAX_WIDTH) return KDA_ERR_UNSUPPORTED;
+    if (C % 8 != 0 || (l2_group != 0 && l2_group != 64 && l2_group != 128) ||
+        (l2_group && C % l2_group != 0))
+        return KDA_ERR_UNSUPPORTED;
+    if (C > 65535 * 2048) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
+    const int64_t total = cu_seqlens ? T_or_total : static_cast<int64_t>(n_seqs) * T_or_total;
+    if (total > kMaxElems / C) return KDA_ERR_SHAPE;
+    if (!weight || (total > 0 && (!x || !y))) return KDA_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(weight) & 3u) ||
+        (reinterpret_cast<uintptr_t>(cache_in) & 3u) || (reinterpret_cast<uintptr_t>(cache_out) & 3u) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)))
+        return KDA_ERR_ALIGN;
+    if (total > 0 && x == y) return KDA_ERR_SHAPE;  // the window reads earlier rows of x
+    kda::ShortConvArgs a{};
+    a.x = x; a.w = weight; a.W = width; a.cache_in = width > 1 ? cache_in : nullptr;
+    a.cache_out = width > 1 ? cache_out : nullptr; a.cu = cu_seqlens; a.n_seqs = n_seqs;
+    a.T = cu_seqlens ? 0 : T_or_total; a.total = total; a.C = C; a.l2 = l2_group; a.y = y;
+    if (total == 0 && !a.cache_out) return KDA_OK;
+    return kda::launch_short_conv(a, dt == KDA_BF16, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -98,7 +98,23 @@ struct OutputGateArgs {
     void* y;            // [rows, dv]
 };
 
+struct ShortConvArgs {
+    const void* x;          // [total, C] projected inputs
+    const float* w;         // [C, W] taps, the last on the current token
+    int W;                  // 1 .. 4
+    const float* cache_in;  // nullable, [N, C, W-1]
+    float* cache_out;       // nullable, [N, C, W-1]; may be cache_in
+    const int32_t* cu;      // nullable => n_seqs sequences of T tokens
+    int n_seqs;
+    int64_t T;
+    int64_t total;
+    int C;
+    int l2;                 // 0, or the channels of one head for L2Norm
+    void* y;                // [total, C]
+};
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+hipError_t launch_short_conv(const ShortConvArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_output_gate(const OutputGateArgs& a, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a, int d, bool bf16, bool commit, hipStream_t stream);

@@ -1,0 +1,185 @@
+// kda_prologue.hip -- KDA input prologue for gfx950: ShortConv + Swish (+ L2Norm per head).
+//
+// [K3 note] = "Kimi K3: Architecture, Training, and Million-Token Agentic RL"
+//   §3.2  q, k = L2Norm(Swish(ShortConv(W x))), v = Swish(ShortConv(W_v x)); in decoding the
+//         layer reads and writes a short-convolution cache C^conv of the few most recent
+//         inputs.  The projections need trained weights; the projected inputs are the input.
+// Readings: causal depthwise convolution of width W (1..4) per channel, the last tap on the
+// current token; history before a sequence's first token from cache_in (oldest first) or
+// zero; Swish(u) = u Sigmoid(u); L2Norm divides each group of l2 channels (one head) by
+// sqrt(sum u^2 + 1e-6); cache_out = the last W - 1 inputs of each sequence.
+//
+// Packed tokens are cut into fixed 32-token segments regardless of sequence boundaries; a
+// segment finds its first token's sequence by binary search and restarts the sliding
+// window whenever it crosses into the next sequence.  Each lane owns 8 consecutive channels
+// (16-byte accesses) and keeps the last W - 1 inputs of them in registers; the L2Norm sum is
+// a butterfly over the lanes of one head.  A second small kernel writes the caches.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+constexpr int kSegT = 32;          // tokens per segment
+constexpr int kChanPerBlock = 2048;  // 256 threads x 8 channels
+
+template <typename T> struct V8;
+template <> struct V8<bf16_t> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float* x) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[2 * i] = lo_bf16(w[i]); x[2 * i + 1] = hi_bf16(w[i]); }
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, const float* x) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+    }
+};
+template <> struct V8<float> {
+    __device__ __forceinline__ static void load(const float* p, float* x) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    __device__ __forceinline__ static void store(float* p, const float* x) {
+        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+};
+
+// sequence containing packed token t (the last sequence whose start is <= t)
+__device__ __forceinline__ int seq_of(const int32_t* cu, int n_seqs, int64_t T, int64_t t) {
+    if (!cu) return static_cast<int>(t / T);
+    int lo = 0, hi = n_seqs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+}  // namespace
+
+template <int W, typename T>
+__global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
+    constexpr int HIST = W - 1;
+    const int c0 = blockIdx.y * kChanPerBlock + threadIdx.x * 8;
+    const bool live = c0 < a.C;
+    const int64_t tb = static_cast<int64_t>(blockIdx.x) * kSegT;
+    const int64_t te = tb + kSegT < a.total ? tb + kSegT : a.total;
+    const T* x = static_cast<const T*>(a.x);
+    T* y = static_cast<T*>(a.y);
+
+    float wt[8][W];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < W; ++i) wt[e][i] = live ? a.w[static_cast<int64_t>(c0 + e) * W + i] : 0.f;
+
+    int n = seq_of(a.cu, a.n_seqs, a.T, tb);
+    int64_t s0 = seq_start(a.cu, a.T, n), s1 = seq_start(a.cu, a.T, n + 1);
+    float win[HIST > 0 ? HIST : 1][8];  // win[i] = input at position t - HIST + i
+    auto fill = [&](int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) {
+            const int64_t p = t - HIST + i;
+            if (p >= s0) {
+                if (live) V8<T>::load(x + p * a.C + c0, win[i]);
+                else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) win[i][e] = 0.f;
+                }
+            } else {
+                const int64_t j = HIST + (p - s0);  // index into this sequence's cache
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    win[i][e] = (a.cache_in && live) ? a.cache_in[(static_cast<int64_t>(n) * a.C + c0 + e) * HIST + j] : 0.f;
+            }
+        }
+    };
+    fill(tb);
+    for (int64_t t = tb; t < te; ++t) {
+        if (t >= s1) {  // crossed into the next non-empty sequence
+            while (seq_start(a.cu, a.T, n + 1) <= t) ++n;
+            s0 = seq_start(a.cu, a.T, n);
+            s1 = seq_start(a.cu, a.T, n + 1);
+            fill(t);
+        }
+        float cur[8], out[8];
+        if (live) V8<T>::load(x + t * a.C + c0, cur);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cur[e] = 0.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = wt[e][HIST] * cur[e];
+#pragma unroll
+            for (int i = 0; i < HIST; ++i) acc += wt[e][i] * win[i][e];
+            out[e] = acc * fast_rcp(1.f + fast_exp2(-acc * kLog2e));  // Swish
+            ss += out[e] * out[e];
+        }
+        if (a.l2 > 0) {
+            for (int off = 1; off < a.l2 / 8; off <<= 1) ss += __shfl_xor(ss, off);
+            const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] *= inv;
+        }
+        if (live) V8<T>::store(y + t * a.C + c0, out);
+#pragma unroll
+        for (int i = 0; i + 1 < HIST; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[i][e] = win[i + 1][e];
+        if (HIST > 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[HIST > 0 ? HIST - 1 : 0][e] = cur[e];
+        }
+    }
+}
+
+// cache_out[n][c][j] = input at position L_n - (W-1) + j of sequence n (from cache_in when
+// that position precedes the sequence); every value is read before any is written, so
+// cache_out may be cache_in.
+template <typename T>
+__global__ void __launch_bounds__(256) conv_cache_kernel(ShortConvArgs a) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<int64_t>(a.n_seqs) * a.C) return;
+    const int n = static_cast<int>(idx / a.C), c = static_cast<int>(idx - static_cast<int64_t>(n) * a.C);
+    const int hist = a.W - 1;
+    const int64_t s0 = seq_start(a.cu, a.T, n), L = seq_start(a.cu, a.T, n + 1) - s0;
+    float v[3];
+    for (int j = 0; j < hist; ++j) {
+        const int64_t p = L - hist + j;
+        v[j] = p >= 0 ? Elem<T>::load1(static_cast<const T*>(a.x) + (s0 + p) * a.C + c)
+                      : (a.cache_in ? a.cache_in[idx * hist + (hist + p)] : 0.f);
+    }
+    for (int j = 0; j < hist; ++j) a.cache_out[idx * hist + j] = v[j];
+}
+
+template <typename T>
+static hipError_t launch_conv_t(const ShortConvArgs& a, hipStream_t stream) {
+    if (a.total > 0) {
+        const dim3 grid(static_cast<unsigned>((a.total + kSegT - 1) / kSegT),
+                        static_cast<unsigned>((a.C + kChanPerBlock - 1) / kChanPerBlock));
+        switch (a.W) {
+            case 1: hipLaunchKernelGGL((short_conv_kernel<1, T>), grid, dim3(256), 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((short_conv_kernel<2, T>), grid, dim3(256), 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((short_conv_kernel<3, T>), grid, dim3(256), 0, stream, a); break;
+            default: hipLaunchKernelGGL((short_conv_kernel<4, T>), grid, dim3(256), 0, stream, a); break;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.cache_out && a.W > 1) {
+        const int64_t n = static_cast<int64_t>(a.n_seqs) * a.C;
+        hipLaunchKernelGGL((conv_cache_kernel<T>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                           stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_short_conv(const ShortConvArgs& a, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_conv_t<bf16_t>(a, stream) : launch_conv_t<float>(a, stream);
+}
+
+}  // namespace kda

@@ -22,7 +22,7 @@ G_MIN = -5.0
 # exported symbols, in the order include/kda.h declares them
 SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd",
            "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_decode_verify",
-           "kda_decode_commit", "kda_output_gate", "kda_status_str")
+           "kda_decode_commit", "kda_output_gate", "kda_short_conv", "kda_status_str")
 MAX_DRAFT = 16
 
 _lib = None
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_commit.restype = i32
     lib.kda_output_gate.argtypes = [i32, vp, vp, vp, f32, i64, i32, vp, vp]
     lib.kda_output_gate.restype = i32
+    lib.kda_short_conv.argtypes = [i32, vp, vp, i32, vp, vp, vp, i32, i64, i32, i32, vp, vp]
+    lib.kda_short_conv.restype = i32
     _lib = lib
     return lib
 
@@ -233,4 +235,28 @@ def kda_output_gate(o, gate, weight, eps: float = 1e-6, y=None, stream=None):
     _check("kda_output_gate", lib.kda_output_gate(
         _dtype_code(o), _ptr(o), _ptr(gate), _ptr(weight), float(eps), rows, dv, _ptr(y),
         _stream(stream)))
+    return y
+
+
+def kda_short_conv(x, weight, cache_in=None, cache_out=None, cu_seqlens=None,
+                   n_seqs: Optional[int] = None, l2_group: int = 0, y=None, stream=None):
+    """y = Swish(ShortConv(x)) (then L2Norm over groups of l2_group channels); x [total, C];
+    weight [C, width] fp32; caches [N, C, width-1] fp32.  Returns y [total, C]."""
+    lib = load_library()
+    total, C = x.shape
+    width = weight.shape[1]
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        T_or_total = total
+    else:
+        N = 1 if n_seqs is None else int(n_seqs)
+        if total % N:
+            raise ValueError("total tokens not divisible by n_seqs")
+        T_or_total = total // N
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(x, weight, cache_in, cache_out, cu_seqlens, y)
+    _check("kda_short_conv", lib.kda_short_conv(
+        _dtype_code(x), _ptr(x), _ptr(weight), width, _ptr(cache_in), _ptr(cache_out),
+        _ptr(cu_seqlens), N, T_or_total, C, int(l2_group), _ptr(y), _stream(stream)))
     return y

@@ -72,6 +72,9 @@ class Oracle:
         lib.kda_oracle_output_gate.argtypes = [_fp, _fp, _fp, ctypes.c_double, ctypes.c_int64,
                                                ctypes.c_int, _dp]
         lib.kda_oracle_output_gate.restype = None
+        lib.kda_oracle_short_conv.argtypes = [_fp, _fp, ctypes.c_int, _fp, _dp, _ip, ctypes.c_int,
+                                              ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp]
+        lib.kda_oracle_short_conv.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [_fp, _fp, _fp, _fp, _fp, _fp, ctypes.c_double,
                                                _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, _ip, ctypes.c_int, _dp,
@@ -194,6 +197,25 @@ class Oracle:
         self.lib.kda_oracle_output_gate(_ptr(o, _fp), _ptr(gate, _fp), _ptr(w, _fp), float(eps),
                                         rows, dv, _ptr(y, _dp))
         return y
+
+    def short_conv(self, x, w, cache_in=None, cu_seqlens=None, l2_group: int = 0):
+        """Causal depthwise conv (width w.shape[1]) + Swish (+ L2Norm over groups) per
+        sequence; x [total, C]; returns (y [total, C], cache_out [N, C, W-1]) in fp64."""
+        x, w = _f32(x), _f32(w)
+        total, C = x.shape
+        Wk = w.shape[1]
+        cu = np.array([0, total], np.int32) if cu_seqlens is None else \
+            np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = len(cu) - 1
+        ci = None if cache_in is None else _f32(cache_in)
+        y = np.empty((total, C), np.float64)
+        co = np.zeros((N, C, max(Wk - 1, 0)), np.float64)
+        rc = self.lib.kda_oracle_short_conv(_ptr(x, _fp), _ptr(w, _fp), Wk, _ptr(ci, _fp),
+                                            _ptr(co, _dp), _ptr(cu, _ip), N, 0, C, int(l2_group),
+                                            _ptr(y, _dp))
+        if rc != 0:
+            raise ValueError(f"kda_oracle_short_conv failed: {rc}")
+        return y, co
 
 
 _default: Optional[Oracle] = None

@@ -364,3 +364,63 @@ void kda_oracle_output_gate(const float *o, const float *gate, const float *w, d
         }
     }
 }
+
+/*
+ * Input prologue ([K3 note] §3.2): q, k = L2Norm(Swish(ShortConv(W x))) and
+ * v = Swish(ShortConv(W_v x)); during decoding ShortConv also reads the layer's short
+ * convolution cache C^conv of the few most recent inputs, and writes it back.  The
+ * projections W x need trained weights, so the projected inputs x arrive as an input.
+ * Readings of what the pages leave open: ShortConv is a causal depthwise convolution over
+ * time of width Wk per channel, out_t[c] = sum_i w[c][i] * x_{t-Wk+1+i}[c] (the last tap
+ * multiplies the current token); inputs before a sequence's first token come from cache_in
+ * (the Wk-1 most recent earlier inputs, oldest first) or are zero; Swish(u) = u Sigmoid(u);
+ * L2Norm divides each group of l2_group channels (one head) by sqrt(sum u^2 + 1e-6).
+ * cache_out receives the last Wk-1 inputs of each sequence, reaching back into cache_in
+ * for short sequences.
+ *
+ * x [total, C] (fp32 values), w [C, Wk], cache_in/out [N, C, Wk-1] (nullable), y [total, C].
+ */
+int kda_oracle_short_conv(const float *x, const float *w, int Wk, const float *cache_in,
+                          double *cache_out, const int32_t *cu, int N, int64_t T, int C,
+                          int l2_group, double *y)
+{
+    if (Wk < 1 || C <= 0 || N <= 0 || (l2_group > 0 && C % l2_group != 0)) return KDA_ORACLE_EINVAL;
+    const int hist = Wk - 1;
+    for (int n = 0; n < N; ++n) {
+        const int64_t s0 = seq_start(cu, T, n), s1 = seq_start(cu, T, n + 1);
+        const int64_t L = s1 - s0;
+        for (int64_t t = 0; t < L; ++t) {
+            double *yrow = y + (s0 + t) * C;
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int i = 0; i < Wk; ++i) {
+                    const int64_t p = t - hist + i;  /* position inside the sequence */
+                    double xv;
+                    if (p >= 0) xv = x[(s0 + p) * C + c];
+                    else xv = cache_in ? cache_in[((int64_t)n * C + c) * hist + (hist + p)] : 0.0;
+                    acc += (double)w[(int64_t)c * Wk + i] * xv;
+                }
+                yrow[c] = acc / (1.0 + exp(-acc));  /* Swish */
+            }
+            if (l2_group > 0) {
+                for (int g0 = 0; g0 < C; g0 += l2_group) {
+                    double ss = 0.0;
+                    for (int c = g0; c < g0 + l2_group; ++c) ss += yrow[c] * yrow[c];
+                    const double inv = 1.0 / sqrt(ss + 1e-6);
+                    for (int c = g0; c < g0 + l2_group; ++c) yrow[c] *= inv;
+                }
+            }
+        }
+        if (cache_out && hist > 0) {
+            for (int c = 0; c < C; ++c)
+                for (int j = 0; j < hist; ++j) {
+                    const int64_t p = L - hist + j;
+                    double xv;
+                    if (p >= 0) xv = x[(s0 + p) * C + c];
+                    else xv = cache_in ? cache_in[((int64_t)n * C + c) * hist + (hist + p)] : 0.0;
+                    cache_out[((int64_t)n * C + c) * hist + j] = xv;
+                }
+        }
+    }
+    return KDA_ORACLE_OK;
+}

@@ -148,6 +148,19 @@ def test_output_gate_rejects_bad_arguments(lib):
     assert og(rows=0, o=None, gate=None, y=None) == OK
 
 
+def test_short_conv_rejects_bad_arguments(lib):
+    def sc(dt=BF16, x=P, w=P, width=4, cin=None, cout=None, cu=None, N=1, T=64, C=256, l2=128, y=ctypes.c_void_p(0x20000)):
+        return lib.kda_short_conv(dt, x, w, width, cin, cout, cu, N, T, C, l2, y, None)
+    assert sc(x=None) == ENULL and sc(w=None) == ENULL and sc(y=None) == ENULL
+    assert sc(width=0) == EUNSUP and sc(width=5) == EUNSUP
+    assert sc(C=260) == EUNSUP                    # not a multiple of 8
+    assert sc(l2=32) == EUNSUP and sc(C=192, l2=128) == EUNSUP
+    assert sc(N=0) == ESHAPE and sc(T=-1) == ESHAPE
+    assert sc(x=MIS) == EALIGN and sc(cu=ctypes.c_void_p(0x10002)) == EALIGN
+    assert sc(y=P) == ESHAPE                      # y must not be x
+    assert sc(T=0) == OK
+
+
 def test_workspace_size_is_aligned(lib):
     for args in [(4096, 1, 16, 128, 128, BF16), (293000, 64, 32, 128, 128, BF16), (256, 1, 2, 64, 64, F32)]:
         assert lib.kda_prefill_workspace_size(*args) % 256 == 0

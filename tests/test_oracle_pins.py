@@ -146,3 +146,73 @@ def test_output_gate_closed_forms(oracle_lib):
                                 np.ones(dv, np.float32), eps=0.0)
     assert np.allclose(y1, y2, rtol=1e-12)
     assert np.allclose((y1 ** 2).mean(axis=1), 1.0, rtol=1e-12)
+
+
+# ---- input prologue: ShortConv + Swish (+ L2Norm) with the convolution cache ----------
+
+def _swish(u):
+    return u / (1.0 + np.exp(-u))
+
+
+def test_short_conv_worked_example(oracle_lib):
+    g = _golden_rows("short_conv_worked_example.txt")
+    x = g[:, 0].astype(np.float32)[:, None]
+    w = np.array([[0.25, 0.5, 1.0]], np.float32)
+    y, co = oracle_lib.short_conv(x, w)
+    assert np.allclose(y[:, 0], _swish(g[:, 1]), rtol=1e-14)
+    assert np.array_equal(co[0, 0], [3.0, 4.0])
+    y, co = oracle_lib.short_conv(x, w, cache_in=np.array([[[10.0, 20.0]]], np.float32))
+    assert np.allclose(y[:, 0], _swish(g[:, 2]), rtol=1e-14)
+    assert np.array_equal(co[0, 0], [3.0, 4.0])
+    # a one-token sequence shifts the cache: (20, x0)
+    y, co = oracle_lib.short_conv(x[:1], w, cache_in=np.array([[[10.0, 20.0]]], np.float32))
+    assert np.array_equal(co[0, 0], [20.0, 1.0])
+    assert np.isclose(y[0, 0], _swish(13.5), rtol=1e-14)
+
+
+def test_short_conv_impulse_and_width_one(oracle_lib):
+    rng = np.random.default_rng(7)
+    C, Wk = 5, 4
+    w = rng.standard_normal((C, Wk)).astype(np.float32)
+    x = np.zeros((6, C), np.float32)
+    x[0] = 1.0
+    y, _ = oracle_lib.short_conv(x, w)
+    # impulse response: pre_t = w[:, Wk-1-t] for t < Wk, then 0
+    for t in range(6):
+        pre = w[:, Wk - 1 - t].astype(np.float64) if t < Wk else np.zeros(C)
+        assert np.allclose(y[t], _swish(pre), rtol=1e-14, atol=0)
+    # width 1 with unit taps: y = Swish(x), no history
+    x = rng.standard_normal((7, C)).astype(np.float32)
+    y, co = oracle_lib.short_conv(x, np.ones((C, 1), np.float32))
+    assert np.allclose(y, _swish(x.astype(np.float64)), rtol=1e-14)
+    assert co.shape == (1, C, 0)
+
+
+def test_short_conv_split_and_l2norm(oracle_lib):
+    rng = np.random.default_rng(8)
+    C, Wk, L = 8, 4, 11
+    w = rng.standard_normal((C, Wk)).astype(np.float32)
+    x = rng.standard_normal((L, C)).astype(np.float32)
+    c0 = rng.standard_normal((1, C, Wk - 1)).astype(np.float32)
+    y_full, co_full = oracle_lib.short_conv(x, w, cache_in=c0)
+    # resuming from the cache after any split reproduces the single call exactly
+    for a in (1, 2, 5, 10):
+        y1, co1 = oracle_lib.short_conv(x[:a], w, cache_in=c0)
+        y2, co2 = oracle_lib.short_conv(x[a:], w, cache_in=co1.astype(np.float32))
+        assert np.array_equal(np.concatenate([y1, y2]), y_full)
+        assert np.array_equal(co2, co_full)
+    # varlen: sequences are independent (each restarts from its own cache)
+    cu = np.array([0, 4, 4, 11], np.int32)
+    cin = rng.standard_normal((3, C, Wk - 1)).astype(np.float32)
+    y_v, co_v = oracle_lib.short_conv(x, w, cache_in=cin, cu_seqlens=cu)
+    for n in range(3):
+        yn, con = oracle_lib.short_conv(x[cu[n]:cu[n + 1]], w, cache_in=cin[n:n + 1]) if cu[n + 1] > cu[n] \
+            else (np.zeros((0, C)), cin[n:n + 1].astype(np.float64))
+        assert np.array_equal(y_v[cu[n]:cu[n + 1]], yn)
+        assert np.array_equal(co_v[n], con[0])
+    # L2Norm: each group of 4 channels has unit norm up to the 1e-6 in the root
+    y_n, _ = oracle_lib.short_conv(x, w, l2_group=4)
+    y_r, _ = oracle_lib.short_conv(x, w)
+    for g0 in (0, 4):
+        nr = np.sqrt((y_r[:, g0:g0 + 4] ** 2).sum(axis=1) + 1e-6)
+        assert np.allclose(y_n[:, g0:g0 + 4], y_r[:, g0:g0 + 4] / nr[:, None], rtol=1e-14)
