@@ -151,11 +151,14 @@ kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* 
     a.blocks = static_cast<char*>(workspace) + table;
     // state pass: enough (sequence, head, dv slice) chains to cover the compute units
     const int cus = compute_units();
-    // d = 128: two workgroups per (sequence, head) (dv slices of 64) while that still fits
-    // the compute units, else one workgroup covering all 128 columns.
-    const int ct = (dk == 128 && 2 * static_cast<int64_t>(a.npairs) > cus) ? 2 : 1;
-    return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ct, stream) == hipSuccess ? KDA_OK
-                                                                                         : KDA_ERR_HIP;
+    // Each state-pass workgroup copies the whole factor block of every chunk, so narrow dv
+    // slices cost block re-reads (from L2: the slices of one head run on one XCD) but shorten
+    // the per-chunk critical path.  Halve the compute waves per workgroup (64 columns at
+    // most) while the chains still fit the compute units.
+    const int64_t np = a.npairs;
+    int ncw = 4;
+    while (ncw > 1 && np * (dk / (8 * ncw)) <= cus) ncw /= 2;
+    return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ncw, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace

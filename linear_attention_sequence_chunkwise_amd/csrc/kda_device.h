@@ -101,6 +101,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
+// The same with 4-byte pieces (256 bytes at lds).
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, 0, 0, 0);
+}
 
 // --- element loads of the caller's tensor type -------------------------------------------
 

@@ -55,8 +55,8 @@ struct SplitArgs : PrefillArgs {
 size_t split_block_bytes(int dk);
 int64_t split_max_chunks(int64_t total, int n_seqs);
 size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk);
-// ct: 16-column state tiles per compute wave; a state-pass workgroup covers 64 ct dv columns
-hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ct, hipStream_t stream);
+// State-pass workgroup shape: ncw (1, 2 or 4) compute waves of 16 dv columns each.
+hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ncw, hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;

@@ -32,7 +32,7 @@
 //   Kt = K~ and Qt = Q~ [64 x DK], KnT = (K e^{Gamma_n - Gamma})^T [DK x 64], each stored as
 //   the lane-order image (lane_off, kn_off) that the state pass copies verbatim into LDS,
 //   T and M as their 10 lower 16x16 blocks (row-major, block order (a,b) = a(a+1)/2 + b),
-//   decayN [DK] fp32 = e^{Gamma_n}.
+//   decayN [DK] fp32 = e^{Gamma_n}; order Qt, M | Kt, KnT, T, decayN (struct Block).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -42,16 +42,20 @@ namespace {
 
 constexpr int kC = 64;  // chunk
 
+// Factor block layout: the operands of the output products (Q~, M) first, then those of the
+// recurrence (K~, K^n, T, e^{Gamma_n}); both parts start on a 1 KiB boundary.
 template <int DK>
 struct Block {
-    static constexpr size_t KT = 0;
-    static constexpr size_t QT = KT + size_t(kC) * DK * 2;
-    static constexpr size_t KN = QT + size_t(kC) * DK * 2;
+    static constexpr size_t QT = 0;
+    static constexpr size_t MB = QT + size_t(kC) * DK * 2;
+    static constexpr size_t KT = MB + 10 * 512;
+    static constexpr size_t KN = KT + size_t(kC) * DK * 2;
     static constexpr size_t TB = KN + size_t(DK) * kC * 2;
-    static constexpr size_t MB = TB + 10 * 512;
-    static constexpr size_t DN = MB + 10 * 512;
+    static constexpr size_t DN = TB + 10 * 512;
     static constexpr size_t BYTES = DN + size_t(DK) * 4;  // multiple of 256
-    static_assert(BYTES % 256 == 0, "block alignment");
+    static constexpr int NQP = static_cast<int>(KT / 1024);            // 1 KiB pieces of Q~, M
+    static constexpr int NBP = static_cast<int>((BYTES + 1023) / 1024);  // pieces of the block
+    static_assert(BYTES % 256 == 0 && KT % 1024 == 0, "block alignment");
 };
 
 __device__ __forceinline__ int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
@@ -524,144 +528,243 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
 }
 
 // ---- K2: serial state pass -----------------------------------------------------------------
-// Eight waves per workgroup: waves 0-3 compute, waves 4-7 copy the next chunk's factor block
-// and v slice from global memory straight into the other half of a double-buffered LDS stage
-// with LDS-DMA loads (buffer_load_dwordx4 ... lds: each instruction writes one contiguous
-// 1 KiB piece, 16 bytes per lane, without passing through registers), while the compute waves
-// work on the current half.  One workgroup barrier per chunk.  The factor block is stored by
-// the intra-chunk kernel in exactly this LDS layout, with the operands of the big products in
-// lane order, so every compute read of them is a linear, conflict-free ds_read_b128.
+// A workgroup runs the chain of one (sequence, head) over a slice of dv columns.  Loader
+// waves copy the next chunk's factor block and v slice from global memory straight into the
+// other half of a double-buffered LDS stage with LDS-DMA loads (buffer_load_dwordx4 ... lds:
+// each instruction writes one contiguous 1 KiB piece, 16 bytes per lane, without passing
+// through registers) while the compute waves work on the current half; one workgroup barrier
+// per chunk.  The factor block is stored by the intra-chunk kernel in exactly this LDS
+// layout, with the operands of the big products in lane order, so every compute read of them
+// is a linear, conflict-free ds_read_b128.
 //
-// Compute wave cw owns dv columns [col0, col0 + 16 CT) of the state, in registers:
-//   Sacc[ct][m][r] = S[pi(m, 4g + r)][col0 + 16 ct + li],
-// so that bf16-packing Sacc[ct][2s], Sacc[ct][2s+1] gives, per lane, the eight channels
-// 32 s + 8 g + e, which is both the B operand of X = K~ S and the A operand of Y^T = S^T Q~^T.
-// O is produced transposed (O^T = Y^T + R^T M^T), which leaves each lane with four adjacent
-// output columns of one token: one 8-byte store per tile, no staging.
+// A compute wave owns 16 dv columns [col0, col0 + 16) of the state, in registers:
+//   S[m][r] = S[pi(m, 4g + r)][col0 + li],
+// so that bf16-packing S[2s], S[2s+1] gives, per lane, the eight channels 32 s + 8 g + e,
+// which is both the B operand of X = K~ S and the A operand of Y^T = S^T Q~^T.  O is produced
+// transposed (O^T = Y^T + R^T M^T), which leaves each lane with four adjacent output columns
+// of one token: one 8-byte store per tile, no staging.
+//
+// Two forms: prefill_state_kernel (NCW compute waves, each running whole chunks for its 16
+// columns) and prefill_state_lagged_kernel (one 16-column slice; the output products on a
+// second wave, one chunk behind).  Narrower slices shorten the per-chunk critical path and
+// make more workgroups read each factor block (from L2).
+// Geometry of a chunk's v slice (DVS columns) in LDS: rows of VRB bytes, VRP rows per
+// 1 KiB piece, pieces VPS bytes apart.
+template <int DVS, typename TIn>
+struct VSlice {
+    static constexpr int VRB = DVS * static_cast<int>(sizeof(TIn));
+    static constexpr int VRP = 1024 / VRB;
+    static constexpr int NVP = kC / VRP;
+    static constexpr int VPS = 1024 + 32;  // padded piece stride: rows 4 apart fall in other banks
+    static constexpr int BYTES = NVP * VPS;
+    static_assert(VRP * VRB == 1024 && NVP * VRP == kC, "v pieces");
+};
+
 template <int DK, int DVS, typename TIn>
 struct StateBuf {
-    static constexpr int NBP = static_cast<int>((Block<DK>::BYTES + 1023) / 1024);  // block pieces
-    static constexpr int VRB = DVS * static_cast<int>(sizeof(TIn));                 // v row bytes
-    static constexpr int VRP = 1024 / VRB;                                          // v rows per piece
-    static constexpr int NVP = kC / VRP;                                            // v pieces
-    static constexpr int VPS = 1024 + 32;  // padded piece stride: rows 4 apart fall in other banks
-    uint4 blk[NBP * 64];                   // the factor block (the last piece may run past it)
-    unsigned char v[NVP * VPS];            // v slice, rows of VRB bytes, VRP rows per piece
+    using V = VSlice<DVS, TIn>;
+    static constexpr int VRB = V::VRB, VRP = V::VRP, VPS = V::VPS;
+    uint4 blk[Block<DK>::NBP * 64];  // the factor block (the last piece may run past it)
+    unsigned char v[V::BYTES];       // v slice, rows of VRB bytes, VRP rows per piece
     float beta[kC];
 };
 
-template <int DK, int CT, typename TIn>
-__global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
-    constexpr int DVS = 64 * CT;  // columns per workgroup (4 compute waves x 16 CT)
+// The (sequence, head, dv slice) chain of one state-pass workgroup.  Consecutive workgroups
+// go to different XCDs, and all slices of one (sequence, head) to the same XCD, where they
+// share the L2 copy of its factor blocks.
+struct ChainPos {
+    int n, h, slice, slot0, nchunks;
+    int64_t tok0, len;
+};
+__device__ __forceinline__ bool chain_pos(const SplitArgs& a, ChainPos& p) {
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, kq = bid >> 3;
+    const int pair = (kq / a.nslices) * 8 + xcd;
+    if (pair >= a.npairs) return false;
+    p.slice = kq % a.nslices;
+    p.n = pair / a.H;
+    p.h = pair - p.n * a.H;
+    if (a.cu) {
+        p.tok0 = a.cu[p.n];
+        p.len = static_cast<int64_t>(a.cu[p.n + 1]) - p.tok0;
+        p.slot0 = a.chunk_start[p.n];
+    } else {
+        p.tok0 = static_cast<int64_t>(p.n) * a.T;
+        p.len = a.T;
+        p.slot0 = p.n * static_cast<int>((a.T + kC - 1) / kC);
+    }
+    p.nchunks = static_cast<int>((p.len + kC - 1) / kC);
+    return true;
+}
+
+// Loader waves of the state pass: NLW waves move the NBP pieces (1 KiB) of a chunk's factor
+// block and the NVP pieces of its v slice into LDS with LDS-DMA copies (16 bytes per lane,
+// not through registers), piece p by wave p mod NLW; block pieces below Block::NQP (Q~, M) go
+// to one destination, the rest (K~, K^n, T, e^{Gamma_n}) to another.  With each chunk's copies
+// they also pull the next chunk's block lines (this slice's share, line slice + nslices m) and
+// v rows into L2 with loads whose results are only folded into a sink at the next fetch, so
+// nothing waits for them: the copies then find their lines in L2 instead of waiting on the
+// farther memory with only one chunk of look-ahead.
+template <int DK, int DVS, typename TIn, int NLW, int TL = 1>
+struct StageLoader {
+    using V = VSlice<DVS, TIn>;
+    using B = Block<DK>;
+    static constexpr int NBP = B::NBP, NQP = B::NQP, NVP = V::NVP, VRP = V::VRP, VRB = V::VRB;
+    static constexpr int LPR = VRB / 16;  // lanes per v row
+    static constexpr int PPW = (NBP + NVP + NLW - 1) / NLW;
+    static constexpr int LINES = static_cast<int>(B::BYTES / 128);
+    static constexpr int TPW = (LINES + 64 * NLW - 1) / (64 * NLW) + 1;  // + 1: v rows
+    const char* blocks;   // factor block of chunk 0 of this (sequence, head)
+    size_t block_stride;  // bytes from one chunk's block to the next
+    const char* v;        // v[tok0][h][first column of the slice]
+    const char* beta;     // beta[tok0][h]
+    int64_t len;
+    uint32_t rowV, rowB;  // bytes per token of v and beta
+    int lw, lane, slice, nslices, nchunks;
+    uint32_t rbr = 0;     // raw beta bits, converted only when stored (a use here would wait)
+
+    __device__ __forceinline__ int chunk_len(int c) const {
+        const int64_t rem = len - static_cast<int64_t>(c) * kC;
+        return rem < kC ? static_cast<int>(rem) : kC;
+    }
+    // Copies of chunk c: block pieces p < NQP to q + 64 p, the others to a + 64 (p - NQP), v
+    // pieces to vdst.  Then the L2 warm-up of chunk c + TL: 4-byte LDS-DMA loads of its lines
+    // into the dummy words `sink` (64 per wave), which nothing reads, so nothing waits for them.
+    __device__ __forceinline__ void fetch(int c, uint4* q, uint4* a, unsigned char* vdst, uint32_t* sink) {
+        const int clen = chunk_len(c);
+        const rsrc_t rf = make_rsrc(blocks + static_cast<size_t>(c) * block_stride, B::BYTES);
+        const rsrc_t rv = make_rsrc(v + static_cast<int64_t>(c) * kC * rowV, clen * rowV);
+        if (lw == 0) {
+            const rsrc_t rbs = make_rsrc(beta + static_cast<int64_t>(c) * kC * rowB, clen * rowB);
+            if constexpr (sizeof(TIn) == 2) rbr = bload2(rbs, lane * rowB);
+            else rbr = bload4(rbs, lane * rowB);
+        }
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
+            const int p = lw + NLW * i;
+            if (p < NQP) {
+                dma16(rf, q + p * 64, p * 1024 + lane * 16);
+            } else if (p < NBP) {
+                dma16(rf, a + (p - NQP) * 64, p * 1024 + lane * 16);
+            } else if (p < NBP + NVP) {
+                const int j = p - NBP;
+                dma16(rv, vdst + j * V::VPS, (j * VRP + lane / LPR) * rowV + (lane % LPR) * 16);
+            }
+        }
+        // warm-up (a no-op past the last chunk: empty ranges load nothing)
+        const int cn = c + TL;
+        const bool live = cn < nchunks;
+        const rsrc_t tf = make_rsrc(blocks + static_cast<size_t>(cn) * block_stride, live ? B::BYTES : 0);
+        const rsrc_t tv = make_rsrc(v + static_cast<int64_t>(cn) * kC * rowV, live ? chunk_len(cn) * rowV : 0);
+#pragma unroll
+        for (int i = 0; i + 1 < TPW; ++i)
+            dma4(tf, sink, static_cast<uint32_t>(slice + nslices * (lane + 64 * (lw + NLW * i))) * 128);
+        dma4(tv, sink, lw == 0 ? lane * rowV : 0x7ffffff0u);
+    }
+    // wait for the copies (the TPW newest loads, the warm-up, may stay in flight) and store beta
+    __device__ __forceinline__ void commit(float* bdst) {
+        // s_waitcnt fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+        __builtin_amdgcn_s_waitcnt((TPW & 15) | (7 << 4) | (15 << 8) | ((TPW >> 4) << 14));
+        if (lw == 0) bdst[lane] = __uint_as_float(sizeof(TIn) == 2 ? rbr << 16 : rbr);
+    }
+    // The loaders' side of the chunk barrier.  A release fence would wait for every LDS-DMA
+    // load, the warm-up included; the copies are already complete (commit), so only the beta
+    // store is waited for here.  The empty asm statements keep the compiler from moving LDS
+    // accesses across the barrier.
+    __device__ __forceinline__ static void barrier() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+};
+
+template <int DK, int DVS, typename TIn, int NLW>
+__device__ __forceinline__ StageLoader<DK, DVS, TIn, NLW> make_loader(const SplitArgs& a, const ChainPos& p, int lw) {
+    using B = Block<DK>;
+    constexpr int ES = static_cast<int>(sizeof(TIn));
+    StageLoader<DK, DVS, TIn, NLW> ld;
+    const int dv = DK;
+    ld.blocks = static_cast<const char*>(a.blocks) + (static_cast<size_t>(p.slot0) * a.H + p.h) * B::BYTES;
+    ld.block_stride = static_cast<size_t>(a.H) * B::BYTES;
+    ld.v = static_cast<const char*>(a.v) +
+           (p.tok0 * a.H * dv + static_cast<int64_t>(p.h) * dv + static_cast<int64_t>(p.slice) * DVS) * ES;
+    ld.beta = static_cast<const char*>(a.beta) + (p.tok0 * a.H + p.h) * ES;
+    ld.len = p.len;
+    ld.rowV = static_cast<uint32_t>(a.H) * dv * ES;
+    ld.rowB = static_cast<uint32_t>(a.H) * ES;
+    ld.lw = lw;
+    ld.lane = threadIdx.x & 63;
+    ld.slice = p.slice;
+    ld.nslices = a.nslices;
+    ld.nchunks = p.nchunks;
+    return ld;
+}
+
+template <int DK, int NCW, int NLW, typename TIn>
+__global__ void __launch_bounds__(64 * (NCW + NLW)) prefill_state_kernel(SplitArgs args) {
+    constexpr int DVS = 16 * NCW;  // columns per workgroup (16 per compute wave)
     using Buf = StateBuf<DK, DVS, TIn>;
-    using P = Pair<TIn>;
     using B = Block<DK>;
     constexpr int KS = DK / 32;
     constexpr int MT = DK / 16;
     constexpr int ES = static_cast<int>(sizeof(TIn));
-    constexpr int NBP = Buf::NBP, NVP = Buf::NVP, VRP = Buf::VRP, VRB = Buf::VRB;
-    constexpr int LPR = VRB / 16;  // lanes per v row
-    static_assert(VRP * VRB == 1024 && NVP * VRP == kC, "v pieces");
+    constexpr int VRP = Buf::VRP, VRB = Buf::VRB;
 
     __shared__ Buf sm[2];
+    __shared__ uint32_t tsink[64];  // target of the loaders' L2 warm-up loads, never read
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, kq = bid >> 3;
-    const int pair = (kq / args.nslices) * 8 + xcd;
-    const int slice = kq % args.nslices;
-    if (pair >= args.npairs) return;
-    const int H = args.H;
-    const int n = pair / H, h = pair - n * H;
-    int64_t tok0, len;
-    int slot0;
-    if (args.cu) {
-        tok0 = args.cu[n];
-        len = static_cast<int64_t>(args.cu[n + 1]) - tok0;
-        slot0 = args.chunk_start[n];
-    } else {
-        tok0 = static_cast<int64_t>(n) * args.T;
-        len = args.T;
-        slot0 = n * static_cast<int>((args.T + kC - 1) / kC);
-    }
-    const int nchunks = static_cast<int>((len + kC - 1) / kC);
+    ChainPos cp;
+    if (!chain_pos(args, cp)) return;
+    const int H = args.H, n = cp.n, h = cp.h, slice = cp.slice, nchunks = cp.nchunks;
+    const int64_t tok0 = cp.tok0, len = cp.len;
     const int dv = DK;
     const uint32_t rowV = static_cast<uint32_t>(H) * dv * ES;
 
-    if (w >= 4) {
+    if (w >= NCW) {
         // ================================ loader waves ================================
-        const int lw = w - 4;
-        const uint32_t rowB = static_cast<uint32_t>(H) * ES;
-        const char* vbase = static_cast<const char*>(args.v) + (static_cast<size_t>(h) * dv + slice * DVS) * ES;
-        const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
-        const char* blocks = static_cast<const char*>(args.blocks);
-        // issue the copies of chunk c into stage b; wave 4 also fetches beta into a register
-        auto issue = [&](int c, Buf& b, float& rb) __attribute__((always_inline)) {
-            const int64_t rem = len - static_cast<int64_t>(c) * kC;
-            const int clen = rem < kC ? static_cast<int>(rem) : kC;
-            const int64_t t0 = tok0 + static_cast<int64_t>(c) * kC;
-            const rsrc_t rf = make_rsrc(blocks + (static_cast<size_t>(slot0 + c) * H + h) * B::BYTES, B::BYTES);
-            for (int p = lw; p < NBP; p += 4)
-                dma16(rf, &b.blk[p * 64], p * 1024 + lane * 16);
-            const rsrc_t rvs = make_rsrc(vbase + t0 * rowV, clen * rowV);
-            for (int j = lw; j < NVP; j += 4)
-                dma16(rvs, &b.v[j * Buf::VPS], (j * VRP + lane / LPR) * rowV + (lane % LPR) * 16);
-            if (lw == 0) {
-                const rsrc_t rbs = make_rsrc(bbase + t0 * rowB, clen * rowB);
-                rb = P::load_beta(rbs, lane * rowB);
-            }
-        };
-        float rb = 0.f;
+        auto ld = make_loader<DK, DVS, TIn, NLW>(args, cp, w - NCW);
         if (nchunks > 0) {
-            issue(0, sm[0], rb);
-            __builtin_amdgcn_s_waitcnt(0);
-            if (lw == 0) sm[0].beta[lane] = rb;
+            ld.fetch(0, sm[0].blk, sm[0].blk + B::NQP * 64, sm[0].v, tsink);
+            ld.commit(sm[0].beta);
         }
-        lds_barrier();
+        ld.barrier();
         for (int c = 0; c < nchunks; ++c) {
             if (c + 1 < nchunks) {
                 Buf& b = sm[(c + 1) & 1];
-                issue(c + 1, b, rb);
-                __builtin_amdgcn_s_waitcnt(0);
-                if (lw == 0) b.beta[lane] = rb;
+                ld.fetch(c + 1, b.blk, b.blk + B::NQP * 64, b.v, tsink);
+                ld.commit(b.beta);
             }
-            lds_barrier();
+            ld.barrier();
         }
         return;
     }
 
     // ================================ compute waves ================================
-    const int col0 = slice * DVS + 16 * CT * w;
+    const int col0 = slice * DVS + 16 * w;
     char* obase = static_cast<char*>(args.o) + (static_cast<size_t>(h) * dv + col0) * ES;
 
-    f32x4_t Sacc[CT][MT];
+    f32x4_t S[MT];
     const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * dv + col0 + li;
     if (args.s0) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Sacc[ct][m][r] = args.s0[sbase + 16 * ct +
-                                             static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv];
+            for (int r = 0; r < 4; ++r)
+                S[m][r] = args.s0[sbase + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv];
     } else {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) Sacc[ct][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MT; ++m) S[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     // this wave's columns of the state to dst = &S[0][col0 + li] of one (sequence, head)
     auto store_state = [&](float* dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[16 * ct + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] = Sacc[ct][m][r];
+            for (int r = 0; r < 4; ++r)
+                dst[static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] = S[m][r];
     };
     lds_barrier();
 
@@ -679,10 +782,7 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
         const int64_t t0 = tok0 + static_cast<int64_t>(c) * kC;
         const rsrc_t ro = make_rsrc(obase + t0 * rowV, clen * rowV);
 
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-        f32x4_t* S = Sacc[ct];
-        const int vc = 16 * CT * w + 16 * ct + li;  // this lane's v column in the slice
+        const int vc = 16 * w + li;  // this lane's v column in the slice
         uint4 Sb[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
@@ -788,11 +888,11 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 S[m] = mfma32(kk[sp][m], make_uint4(Ub[2 * sp].x, Ub[2 * sp].y, Ub[2 * sp + 1].x, Ub[2 * sp + 1].y), S[m]);
-        // O: Ot[r] = O[16a + li][col0 + 16ct + 4g + r]
+        // O: Ot[r] = O[16a + li][col0 + 4g + r]
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const f32x4_t Ot = Om[a] + Yt[a];
-            const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + (16 * ct + 4 * g) * ES;
+            const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + 4 * g * ES;
             if constexpr (sizeof(TIn) == 2) {
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])},
                                                       ro, off, 0, 0);
@@ -801,13 +901,263 @@ __global__ void __launch_bounds__(512) prefill_state_kernel(SplitArgs args) {
                                              __float_as_uint(Ot[2]), __float_as_uint(Ot[3])));
             }
         }
-        }  // column tile
         // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
         if (args.ckpt && (c + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(c + 1) * kC <= len) {
             const int j = (c + 1) / args.ckpt_chunks - 1;
             const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
             store_state(args.ckpt + ((first + j) * H + h) * DK * dv + col0 + li);
         }
+        lds_barrier();
+    }
+
+    if (args.sN) store_state(args.sN + sbase);
+}
+
+// Lagged state pass for 16-column slices: the outputs leave the serial chain.  Wave 0 (chain)
+// runs the recurrence X = K~ S, R = beta (V - X), U = T R, S' = diag(e^{Gamma_n}) S + K^n^T U
+// over chunk c while wave 1 (output) forms O = Q~ S + M R of chunk c - 1 from the chain's
+// packed S and R of that chunk, handed over in LDS -- the output products run on another SIMD
+// one chunk behind, and one barrier per chunk still orders everything.  Buffers live as long
+// as that needs: the recurrence part of the factor block, v and beta in two stages (chunk
+// c + 1 lands while c runs), the Q~/M part and the packed S in three (chunk c - 1 is read while
+// c + 1 lands / S(c + 1) is written), R in two.
+template <int DK, typename TIn>
+struct LagBuf {
+    using V = VSlice<16, TIn>;
+    using B = Block<DK>;
+    static constexpr int NAP = B::NBP - B::NQP;  // pieces of K~, K^n, T, e^{Gamma_n}
+    struct Stage {
+        uint4 a[NAP * 64];
+        unsigned char v[V::BYTES];
+        float beta[kC];
+    };
+    Stage st[2];
+    uint4 q[3][B::NQP * 64];   // Q~, M
+    uint4 xs[3][DK / 32 * 64]; // packed S of a chunk start, in the chain wave's lane order
+    uint2 xr[2][4 * 64];       // packed R, in the chain wave's lane order
+    uint32_t tsink[64];        // target of the loaders' L2 warm-up loads, never read
+};
+
+template <int DK, int NLW, typename TIn>
+__global__ void __launch_bounds__(64 * (2 + NLW)) prefill_state_lagged_kernel(SplitArgs args) {
+    using L = LagBuf<DK, TIn>;
+    using V = VSlice<16, TIn>;
+    using B = Block<DK>;
+    constexpr int KS = DK / 32;
+    constexpr int MT = DK / 16;
+    constexpr int ES = static_cast<int>(sizeof(TIn));
+    // piece offsets (uint4 units) of the recurrence operands inside a stage's a[]
+    constexpr int OKT = 0, OKN = (B::KN - B::KT) / 16, OTB = (B::TB - B::KT) / 16, ODN = (B::DN - B::KT) / 16;
+
+    __shared__ L sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+    ChainPos cp;
+    if (!chain_pos(args, cp)) return;
+    const int H = args.H, n = cp.n, h = cp.h, nchunks = cp.nchunks;
+    const int64_t tok0 = cp.tok0, len = cp.len;
+    const int dv = DK;
+    const uint32_t rowV = static_cast<uint32_t>(H) * dv * ES;
+    const int col0 = cp.slice * 16;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+    if (w >= 2) {
+        // ================================ loader waves ================================
+        auto ld = make_loader<DK, 16, TIn, NLW>(args, cp, w - 2);
+        if (nchunks > 0) {
+            ld.fetch(0, sm.q[0], sm.st[0].a, sm.st[0].v, sm.tsink);
+            ld.commit(sm.st[0].beta);
+        }
+        ld.barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                typename L::Stage& b = sm.st[(c + 1) & 1];
+                ld.fetch(c + 1, sm.q[(c + 1) % 3], b.a, b.v, sm.tsink);
+                ld.commit(b.beta);
+            }
+            ld.barrier();
+        }
+        return;
+    }
+
+    if (w == 1) {
+        // ================================ output wave ================================
+        char* obase = static_cast<char*>(args.o) + (static_cast<size_t>(h) * dv + col0) * ES;
+        // O of chunk e: O^T = S^T Q~^T + R^T M^T
+        auto out = [&](int e) __attribute__((always_inline)) {
+            const uint4* qt = sm.q[e % 3] + B::QT / 16;
+            const uint2* mb = reinterpret_cast<const uint2*>(sm.q[e % 3] + B::MB / 16);
+            const int64_t rem = len - static_cast<int64_t>(e) * kC;
+            const int clen = rem < kC ? static_cast<int>(rem) : kC;
+            const rsrc_t ro = make_rsrc(obase + (tok0 + static_cast<int64_t>(e) * kC) * rowV, clen * rowV);
+            uint4 Sb[KS], opd[4][KS];
+            uint2 Rb[4], mv[10];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) Sb[s] = sm.xs[e % 3][s * 64 + lane];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) opd[a][s] = qt[(a * KS + s) * 64 + lane];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Rb[a] = sm.xr[e & 1][a * 64 + lane];
+#pragma unroll
+            for (int t = 0; t < 10; ++t) mv[t] = mb[t * 64 + li * 4 + g];
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t Yt[4] = {zero, zero, zero, zero}, Om[4] = {zero, zero, zero, zero};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) Yt[a] = mfma32(Sb[s], opd[a][s], Yt[a]);
+            // the M R chain starts from zero and Y^T is added on the VALU, so no accumulator
+            // passes from a 16x16x32 product to a 16x16x16 one
+#pragma unroll
+            for (int bq = 0; bq < 4; ++bq)
+#pragma unroll
+                for (int a = bq; a < 4; ++a) Om[a] = mfma16(Rb[bq], mv[tri_index(a, bq)], Om[a]);
+            // Ot[r] = O[16a + li][col0 + 4g + r]
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4_t Ot = Om[a] + Yt[a];
+                const uint32_t off = static_cast<uint32_t>(16 * a + li) * rowV + 4 * g * ES;
+                if constexpr (sizeof(TIn) == 2) {
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])}, ro, off, 0, 0);
+                } else {
+                    bstore16(ro, off, make_uint4(__float_as_uint(Ot[0]), __float_as_uint(Ot[1]),
+                                                 __float_as_uint(Ot[2]), __float_as_uint(Ot[3])));
+                }
+            }
+        };
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c > 0) out(c - 1);
+            lds_barrier();
+        }
+        if (nchunks > 0) out(nchunks - 1);
+        return;
+    }
+
+    // ================================ chain wave ================================
+    f32x4_t S[MT];
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * dv + col0 + li;
+    // state row of accumulator element (m, r): 32 (m / 2) + 8 g + 4 (m % 2) + r
+    if (args.s0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[m][r] = args.s0[sbase + static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv];
+    } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) S[m] = zero;
+    }
+    auto store_state = [&](float* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[static_cast<size_t>(32 * (m >> 1) + 8 * g + 4 * (m & 1) + r) * dv] = S[m][r];
+    };
+    // packed bf16 state: the B operand of X = K~ S here, the A operand of Y^T in the output wave
+    uint4 Sb[KS];
+    auto pack_state = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            Sb[s] = make_uint4(pack_bf16x2(S[2 * s][0], S[2 * s][1]), pack_bf16x2(S[2 * s][2], S[2 * s][3]),
+                               pack_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]),
+                               pack_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]));
+            sm.xs[slot][s * 64 + lane] = Sb[s];
+        }
+    };
+    pack_state(0);
+    lds_barrier();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const typename L::Stage& b = sm.st[c & 1];
+        const uint4* kt = b.a + OKT;
+        const uint4* kn = b.a + OKN;
+        const uint2* tb = reinterpret_cast<const uint2*>(b.a + OTB);
+        const float* dnv = reinterpret_cast<const float*>(b.a + ODN);
+        uint4 opd[4][KS];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) opd[a][s] = kt[(a * KS + s) * 64 + lane];
+        float vv[4][4];  // v[16a + 4g + r][col li]
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * a + 4 * g + r;
+                const unsigned char* vp = b.v + (row / V::VRP) * V::VPS + (row % V::VRP) * V::VRB + li * ES;
+                if constexpr (sizeof(TIn) == 2) vv[a][r] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(vp));
+                else vv[a][r] = *reinterpret_cast<const float*>(vp);
+            }
+        float4 bb[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) bb[a] = *reinterpret_cast<const float4*>(&b.beta[16 * a + 4 * g]);
+        uint2 tv[10];
+#pragma unroll
+        for (int t = 0; t < 10; ++t) tv[t] = tb[t * 64 + li * 4 + g];
+        __builtin_amdgcn_sched_barrier(0);
+        // X = K~ S: X[a][r] = X[16a + 4g + r][col li], four interleaved chains
+        f32x4_t X[4] = {zero, zero, zero, zero};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) X[a] = mfma32(opd[a][s], Sb[s], X[a]);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 kk[2][MT];
+        float4 dn[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            kk[0][m] = kn[(m * 2 + 0) * 64 + lane];
+            kk[1][m] = kn[(m * 2 + 1) * 64 + lane];
+            dn[m] = *reinterpret_cast<const float4*>(&dnv[32 * (m >> 1) + 8 * g + 4 * (m & 1)]);
+        }
+        // R = beta (V - X).  Rows past the chunk's end are zero without a test: the v copy
+        // writes zeros there, beta reads as zero, and K~ rows are zero, so X is zero too.
+        uint2 Rb[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f32x4_t R;
+            R[0] = bb[a].x * (vv[a][0] - X[a][0]);
+            R[1] = bb[a].y * (vv[a][1] - X[a][1]);
+            R[2] = bb[a].z * (vv[a][2] - X[a][2]);
+            R[3] = bb[a].w * (vv[a][3] - X[a][3]);
+            Rb[a] = pack_bf16x4(R);  // lane: R[16a + 4g + r][col li]
+            sm.xr[c & 1][a * 64 + lane] = Rb[a];
+        }
+        // U = T R, chains over the source tile
+        f32x4_t U[4] = {zero, zero, zero, zero};
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq)
+#pragma unroll
+            for (int a = bq; a < 4; ++a) U[a] = mfma16(tv[tri_index(a, bq)], Rb[bq], U[a]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            S[m][0] *= dn[m].x;
+            S[m][1] *= dn[m].y;
+            S[m][2] *= dn[m].z;
+            S[m][3] *= dn[m].w;
+        }
+        uint2 Ub[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) Ub[a] = pack_bf16x4(U[a]);
+        // S = diag(e^{Gamma_n}) S + K^n^T U
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                S[m] = mfma32(kk[sp][m], make_uint4(Ub[2 * sp].x, Ub[2 * sp].y, Ub[2 * sp + 1].x, Ub[2 * sp + 1].y), S[m]);
+        // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
+        if (args.ckpt && (c + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(c + 1) * kC <= len) {
+            const int jc = (c + 1) / args.ckpt_chunks - 1;
+            const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
+            store_state(args.ckpt + ((first + jc) * H + h) * DK * dv + col0 + li);
+        }
+        pack_state((c + 1) % 3);
         lds_barrier();
     }
 
@@ -825,8 +1175,10 @@ size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk) {
     return table + static_cast<size_t>(split_max_chunks(total, n_seqs)) * H * split_block_bytes(dk);
 }
 
-template <int DK, int CT, typename TIn>
+// K1 then K2 (the lagged 16-column state pass, or NCW compute waves of 16 columns)
+template <int DK, int NCW, typename TIn, bool LAG = false>
 static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
+    constexpr int NLW = 4;  // loader waves
     SplitArgs a = a0;
     if (a.cu) {
         hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.n_seqs, a.chunk_start);
@@ -841,20 +1193,29 @@ static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    a.nslices = DK / (64 * CT);
+    a.nslices = DK / (16 * NCW);
     const int groups = (a.npairs + 7) / 8;
-    hipLaunchKernelGGL((prefill_state_kernel<DK, CT, TIn>), dim3(static_cast<unsigned>(groups) * 8u * a.nslices),
-                       dim3(512), 0, stream, a);
+    const dim3 grid(static_cast<unsigned>(groups) * 8u * a.nslices);
+    if constexpr (LAG)
+        hipLaunchKernelGGL((prefill_state_lagged_kernel<DK, NLW, TIn>), grid, dim3(64 * (2 + NLW)), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_state_kernel<DK, NCW, NLW, TIn>), grid, dim3(64 * (NCW + NLW)), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ct, hipStream_t stream) {
-    if (dk == 128) {
-        // fp32 v rows of 128 columns would not fit two LDS stages: fp32 uses slices of 64
-        if (ct == 2 && bf16) return launch_split_t<128, 2, bf16_t>(a, stream);
-        return bf16 ? launch_split_t<128, 1, bf16_t>(a, stream) : launch_split_t<128, 1, float>(a, stream);
-    }
-    return bf16 ? launch_split_t<64, 1, bf16_t>(a, stream) : launch_split_t<64, 1, float>(a, stream);
+template <int DK, typename TIn>
+static hipError_t launch_split_d(const SplitArgs& a, int ncw, hipStream_t stream) {
+    // the lagged pass holds three Q~/M stages, which leave no LDS for fp32 v rows at d = 128
+    if constexpr (DK == 64 || sizeof(TIn) == 2)
+        if (ncw == 1) return launch_split_t<DK, 1, TIn, true>(a, stream);
+    if (ncw == 1) return launch_split_t<DK, 1, TIn>(a, stream);
+    if (ncw == 2) return launch_split_t<DK, 2, TIn>(a, stream);
+    return launch_split_t<DK, 4, TIn>(a, stream);
+}
+
+hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ncw, hipStream_t stream) {
+    if (dk == 128) return bf16 ? launch_split_d<128, bf16_t>(a, ncw, stream) : launch_split_d<128, float>(a, ncw, stream);
+    return bf16 ? launch_split_d<64, bf16_t>(a, ncw, stream) : launch_split_d<64, float>(a, ncw, stream);
 }
 
 }  // namespace kda
