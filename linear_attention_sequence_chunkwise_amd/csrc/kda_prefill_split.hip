@@ -175,23 +175,34 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* cu, in
 // scan across the 16 lanes of a DPP row, K~ and Q~ leave registers as linear 1 KiB lane-order
 // writes, and only the column operands (read by other waves) and K^n (transposed for the
 // state pass) go through LDS.
+// Buffers whose lifetimes do not overlap share storage (36 KiB at d = 128: four workgroups
+// fit a CU's LDS): the K^n staging gives way to the tile products once it has been copied out,
+// and the column operand to T and M once the tile products have read it.
 template <int DK>
 struct IntraSmem {
     static constexpr int KS = DK / 32;
     static constexpr int NROW = DK + 8;  // K^n staging rows (bf16), 16-byte aligned
+    struct Tiles {
+        float Ld[4][16][20];        // diagonal blocks of A_kk (fp32), [block][col j][row i]
+        bf16_t L[10][16][16];       // A_kk lower blocks (off-diagonal ones used), row-major
+        bf16_t Aqk[10][16][16];     // A_qk lower blocks, diagonal included
+    };
     struct Out {
         bf16_t T[10][16][16];   // T lower 16x16 blocks, row-major
         bf16_t Tt[10][16][16];  // the same blocks transposed
         bf16_t M[10][16][16];   // M = A_qk T lower blocks, row-major
     };
-    uint4 kc[4 * KS * 64];      // k_j e^{rho_{b+1} - Gamma_j} in lane order [b][s][lane]
-    union { bf16_t kn[kC][NROW]; Out out; } u;  // K^n = K e^{Gamma_n - Gamma} (token-major), later T, M
+    union {
+        bf16_t kn[kC][NROW];    // K^n = K e^{Gamma_n - Gamma} (token-major), until copied out
+        Tiles t;
+    } a;
+    union {
+        uint4 kc[4 * KS * 64];  // k_j e^{rho_{b+1} - Gamma_j} in lane order [b][s][lane]
+        Out out;
+    } b;
     float ttile[4][DK];         // e^{rho_{a+1} - rho_a}: the product of alpha over tile a
     float ae[DK];               // -e^{A} log2(e)
     float beta[kC];
-    float Ld[4][16][20];        // diagonal blocks of A_kk (fp32), [block][col j][row i]
-    bf16_t L[10][16][16];       // A_kk lower blocks (off-diagonal ones used), row-major
-    bf16_t Aqk[10][16][16];     // A_qk lower blocks, diagonal included
 };
 
 // x[lane - n] within the lane's row of 16, or 1 for the first n lanes of the row.
@@ -208,7 +219,7 @@ __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
 }
 
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_kernel(SplitArgs args) {
+__global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_kernel(SplitArgs args) {
     using Smem = IntraSmem<DK>;
     using P = Pair<TIn>;
     using B = Block<DK>;
@@ -326,56 +337,61 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int ch = 32 * s + 8 * g;
-        float Tt[4][8];
+        // two halves of the lane's eight channels (fewer values live at once)
+        uint32_t pkr[4], pqr[4], pkc[4], pkt[4], pqt[4], pkn[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const float4 x0 = *reinterpret_cast<const float4*>(&sm.ttile[a][ch]);
-            const float4 x1 = *reinterpret_cast<const float4*>(&sm.ttile[a][ch + 4]);
-            Tt[a][0] = x0.x; Tt[a][1] = x0.y; Tt[a][2] = x0.z; Tt[a][3] = x0.w;
-            Tt[a][4] = x1.x; Tt[a][5] = x1.y; Tt[a][6] = x1.z; Tt[a][7] = x1.w;
-        }
-        float vkr[8], vqr[8], vkc[8], vkt[8], vqt[8], vkn[8], vdn[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float tw = Tt[0][e], eR = 1.f, eN = 1.f;
-#pragma unroll
-            for (int a = 1; a < 4; ++a) tw = w == a ? Tt[a][e] : tw;
+        for (int hh = 0; hh < 2; ++hh) {
+            float Tt[4][4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                eR *= a < w ? Tt[a][e] : 1.f;
-                eN *= a > w ? Tt[a][e] : 1.f;
+                const float4 x = *reinterpret_cast<const float4*>(&sm.ttile[a][ch + 4 * hh]);
+                Tt[a][0] = x.x; Tt[a][1] = x.y; Tt[a][2] = x.z; Tt[a][3] = x.w;
             }
-            const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
-            const float f = F[s][e];
-            const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
-            vkr[e] = kf * f;
-            vqr[e] = qf * f;
-            vkc[e] = kf * E;
-            vkt[e] = vkr[e] * eR;
-            vqt[e] = vqr[e] * eR;
-            vkn[e] = vkc[e] * eN;
-            vdn[e] = Tt[0][e] * Tt[1][e] * Tt[2][e] * Tt[3][e];
+            float vkr[4], vqr[4], vkc[4], vkt[4], vqt[4], vkn[4];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int e = 4 * hh + e4;
+                float tw = Tt[0][e4], eR = 1.f, eN = 1.f;
+#pragma unroll
+                for (int a = 1; a < 4; ++a) tw = w == a ? Tt[a][e4] : tw;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    eR *= a < w ? Tt[a][e4] : 1.f;
+                    eN *= a > w ? Tt[a][e4] : 1.f;
+                }
+                const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
+                const float f = F[s][e];
+                const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
+                vkr[e4] = kf * f;
+                vqr[e4] = qf * f;
+                vkc[e4] = kf * E;
+                vkt[e4] = vkr[e4] * eR;
+                vqt[e4] = vqr[e4] * eR;
+                vkn[e4] = vkc[e4] * eN;
+            }
+#pragma unroll
+            for (int p2 = 0; p2 < 2; ++p2) {
+                pkr[2 * hh + p2] = pack_bf16x2(vkr[2 * p2], vkr[2 * p2 + 1]);
+                pqr[2 * hh + p2] = pack_bf16x2(vqr[2 * p2], vqr[2 * p2 + 1]);
+                pkc[2 * hh + p2] = pack_bf16x2(vkc[2 * p2], vkc[2 * p2 + 1]);
+                pkt[2 * hh + p2] = pack_bf16x2(vkt[2 * p2], vkt[2 * p2 + 1]);
+                pqt[2 * hh + p2] = pack_bf16x2(vqt[2 * p2], vqt[2 * p2 + 1]);
+                pkn[2 * hh + p2] = pack_bf16x2(vkn[2 * p2], vkn[2 * p2 + 1]);
+            }
+            if (w == 0 && li == 0) {  // e^{Gamma_n}: the product of all four tiles
+                *reinterpret_cast<float4*>(blk + B::DN + (ch + 4 * hh) * 4) =
+                    make_float4(Tt[0][0] * Tt[1][0] * Tt[2][0] * Tt[3][0], Tt[0][1] * Tt[1][1] * Tt[2][1] * Tt[3][1],
+                                Tt[0][2] * Tt[1][2] * Tt[2][2] * Tt[3][2], Tt[0][3] * Tt[1][3] * Tt[2][3] * Tt[3][3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        kr[s] = make_uint4(pack_bf16x2(vkr[0], vkr[1]), pack_bf16x2(vkr[2], vkr[3]), pack_bf16x2(vkr[4], vkr[5]),
-                           pack_bf16x2(vkr[6], vkr[7]));
-        qr[s] = make_uint4(pack_bf16x2(vqr[0], vqr[1]), pack_bf16x2(vqr[2], vqr[3]), pack_bf16x2(vqr[4], vqr[5]),
-                           pack_bf16x2(vqr[6], vqr[7]));
+        kr[s] = make_uint4(pkr[0], pkr[1], pkr[2], pkr[3]);
+        qr[s] = make_uint4(pqr[0], pqr[1], pqr[2], pqr[3]);
         const int piece = (w * KS + s) * 64 + lane;
-        sm.kc[piece] = make_uint4(pack_bf16x2(vkc[0], vkc[1]), pack_bf16x2(vkc[2], vkc[3]),
-                                  pack_bf16x2(vkc[4], vkc[5]), pack_bf16x2(vkc[6], vkc[7]));
-        *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) =
-            make_uint4(pack_bf16x2(vkt[0], vkt[1]), pack_bf16x2(vkt[2], vkt[3]), pack_bf16x2(vkt[4], vkt[5]),
-                       pack_bf16x2(vkt[6], vkt[7]));
-        *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) =
-            make_uint4(pack_bf16x2(vqt[0], vqt[1]), pack_bf16x2(vqt[2], vqt[3]), pack_bf16x2(vqt[4], vqt[5]),
-                       pack_bf16x2(vqt[6], vqt[7]));
-        *reinterpret_cast<uint4*>(&sm.u.kn[r][ch]) =
-            make_uint4(pack_bf16x2(vkn[0], vkn[1]), pack_bf16x2(vkn[2], vkn[3]), pack_bf16x2(vkn[4], vkn[5]),
-                       pack_bf16x2(vkn[6], vkn[7]));
-        if (w == 0 && li == 0) {
-            *reinterpret_cast<float4*>(blk + B::DN + ch * 4) = make_float4(vdn[0], vdn[1], vdn[2], vdn[3]);
-            *reinterpret_cast<float4*>(blk + B::DN + ch * 4 + 16) = make_float4(vdn[4], vdn[5], vdn[6], vdn[7]);
-        }
+        sm.b.kc[piece] = make_uint4(pkc[0], pkc[1], pkc[2], pkc[3]);
+        *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) = make_uint4(pkt[0], pkt[1], pkt[2], pkt[3]);
+        *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) = make_uint4(pqt[0], pqt[1], pqt[2], pqt[3]);
+        *reinterpret_cast<uint4*>(&sm.a.kn[r][ch]) = make_uint4(pkn[0], pkn[1], pkn[2], pkn[3]);
     }
     lds_barrier();
 
@@ -391,10 +407,11 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int t = ta + 16 * hh + 2 * e;
-                wv[2 * hh + e] = static_cast<uint32_t>(sm.u.kn[t][c]) | (static_cast<uint32_t>(sm.u.kn[t + 1][c]) << 16);
+                wv[2 * hh + e] = static_cast<uint32_t>(sm.a.kn[t][c]) | (static_cast<uint32_t>(sm.a.kn[t + 1][c]) << 16);
             }
         *reinterpret_cast<uint4*>(blk + B::KN + p * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
+    lds_barrier();  // the tile products below overwrite the K^n staging
 
     // ---- lower 16x16 tiles (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
     // carries e^{rho_{b+1} - Gamma_j}; it is rescaled per channel by e^{rho_w - rho_{b+1}}
@@ -407,7 +424,7 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const int ch = 32 * s + 8 * g;
-                uint4 col = sm.kc[(b * KS + s) * 64 + lane];
+                uint4 col = sm.b.kc[(b * KS + s) * 64 + lane];
                 if (b != w - 1) {
                     float4 s0, s1;
                     if (b == w) {
@@ -436,15 +453,15 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int jj = 4 * g + rr;
-                    sm.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
+                    sm.a.t.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
                     qv[rr] = jj <= li ? cqk[rr] : 0.f;                // lower incl. diagonal
                 }
-                *reinterpret_cast<uint2*>(&sm.Aqk[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.a.t.Aqk[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
             } else {
-                *reinterpret_cast<uint2*>(&sm.L[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.a.t.L[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(bi * ckk[0], bi * ckk[1]), pack_bf16x2(bi * ckk[2], bi * ckk[3]));
-                *reinterpret_cast<uint2*>(&sm.Aqk[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&sm.a.t.Aqk[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(cqk[0], cqk[1]), pack_bf16x2(cqk[2], cqk[3]));
             }
         }
@@ -462,7 +479,7 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
             float Lm[16];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(&sm.Ld[a][m][4 * q4]);
+                const float4 v4 = *reinterpret_cast<const float4*>(&sm.a.t.Ld[a][m][4 * q4]);
                 Lm[4 * q4] = v4.x; Lm[4 * q4 + 1] = v4.y; Lm[4 * q4 + 2] = v4.z; Lm[4 * q4 + 3] = v4.w;
             }
             const float tm = t[m];
@@ -472,10 +489,10 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
         // column j of T_aa -> T block (row-major) and its transpose (row j)
         const int d = tri_index(a, a);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.u.out.T[d][i][j] = f32_to_bf16(t[i]);
+        for (int i = 0; i < 16; ++i) sm.b.out.T[d][i][j] = f32_to_bf16(t[i]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<uint2*>(&sm.u.out.Tt[d][j][4 * q4]) =
+            *reinterpret_cast<uint2*>(&sm.b.out.Tt[d][j][4 * q4]) =
                 make_uint2(pack_bf16x2(t[4 * q4], t[4 * q4 + 1]), pack_bf16x2(t[4 * q4 + 2], t[4 * q4 + 3]));
     }
     lds_barrier();
@@ -487,15 +504,15 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
         for (int a = b + 1; a < 4; ++a) {
             f32x4_t acc = zero;
             for (int m = b; m < a; ++m)
-                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.L[tri_index(a, m)][li][4 * g]),
-                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[tri_index(m, b)][li][4 * g]), acc);
-            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.u.out.T[tri_index(a, a)][li][4 * g]),
+                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.a.t.L[tri_index(a, m)][li][4 * g]),
+                             *reinterpret_cast<const uint2*>(&sm.b.out.Tt[tri_index(m, b)][li][4 * g]), acc);
+            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.b.out.T[tri_index(a, a)][li][4 * g]),
                                        pack_bf16x4(acc), zero);
             // tab[rr] = -T_ab[4g + rr][li]
             const int d = tri_index(a, b);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.u.out.T[d][4 * g + rr][li] = f32_to_bf16(-tab[rr]);
-            *reinterpret_cast<uint2*>(&sm.u.out.Tt[d][li][4 * g]) =
+            for (int rr = 0; rr < 4; ++rr) sm.b.out.T[d][4 * g + rr][li] = f32_to_bf16(-tab[rr]);
+            *reinterpret_cast<uint2*>(&sm.b.out.Tt[d][li][4 * g]) =
                 make_uint2(pack_bf16x2(-tab[0], -tab[1]), pack_bf16x2(-tab[2], -tab[3]));
         }
     }
@@ -510,10 +527,10 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
             const int b = job - (a * (a + 1)) / 2;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             for (int m = b; m <= a; ++m)
-                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.Aqk[tri_index(a, m)][li][4 * g]),
-                             *reinterpret_cast<const uint2*>(&sm.u.out.Tt[tri_index(m, b)][li][4 * g]), acc);
+                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.a.t.Aqk[tri_index(a, m)][li][4 * g]),
+                             *reinterpret_cast<const uint2*>(&sm.b.out.Tt[tri_index(m, b)][li][4 * g]), acc);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.u.out.M[job][4 * g + rr][li] = f32_to_bf16(acc[rr]);
+            for (int rr = 0; rr < 4; ++rr) sm.b.out.M[job][4 * g + rr][li] = f32_to_bf16(acc[rr]);
         }
     }
     lds_barrier();
@@ -521,8 +538,8 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) prefill_intra_k
     // ---- T and M lower blocks -> factor block (512 bytes per block, 16-byte pieces) -------
     for (int idx = tid; idx < 2 * 10 * 32; idx += NT) {
         const int which = idx / 320, rem = idx % 320;
-        const uint4* src = which == 0 ? reinterpret_cast<const uint4*>(&sm.u.out.T[0][0][0])
-                                      : reinterpret_cast<const uint4*>(&sm.u.out.M[0][0][0]);
+        const uint4* src = which == 0 ? reinterpret_cast<const uint4*>(&sm.b.out.T[0][0][0])
+                                      : reinterpret_cast<const uint4*>(&sm.b.out.M[0][0][0]);
         *reinterpret_cast<uint4*>(blk + (which == 0 ? B::TB : B::MB) + rem * 16) = src[rem];
     }
 }
