@@ -9,7 +9,7 @@
 // zero; Swish(u) = u Sigmoid(u); L2Norm divides each group of l2 channels (one head) by
 // sqrt(sum u^2 + 1e-6); cache_out = the last W - 1 inputs of each sequence.
 //
-// Packed tokens are cut into fixed 32-token segments regardless of sequence boundaries; a
+// Packed tokens are cut into fixed 64-token segments regardless of sequence boundaries; a
 // segment finds its first token's sequence by binary search and restarts the sliding
 // window whenever it crosses into the next sequence.  Each lane owns 8 consecutive channels
 // (16-byte accesses) and keeps the last W - 1 inputs of them in registers; the L2Norm sum is
@@ -20,27 +20,33 @@
 namespace kda {
 
 namespace {
-constexpr int kSegT = 32;          // tokens per segment
+constexpr int kSegT = 64;          // tokens per segment
 constexpr int kChanPerBlock = 2048;  // 256 threads x 8 channels
 
 template <typename T> struct V8;
 template <> struct V8<bf16_t> {
-    __device__ __forceinline__ static void load(const bf16_t* p, float* x) {
-        const uint4 u = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    struct Raw { uint4 a; };  // eight channels as loaded, converted later (a use would wait)
+    __device__ __forceinline__ static Raw load_raw(const bf16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
+    __device__ __forceinline__ static void convert(const Raw& r, float* x) {
+        const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) { x[2 * i] = lo_bf16(w[i]); x[2 * i + 1] = hi_bf16(w[i]); }
     }
+    __device__ __forceinline__ static void load(const bf16_t* p, float* x) { convert(load_raw(p), x); }
     __device__ __forceinline__ static void store(bf16_t* p, const float* x) {
         *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
     }
 };
 template <> struct V8<float> {
-    __device__ __forceinline__ static void load(const float* p, float* x) {
-        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    struct Raw { float4 a, b; };
+    __device__ __forceinline__ static Raw load_raw(const float* p) {
+        return Raw{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
     }
+    __device__ __forceinline__ static void convert(const Raw& r, float* x) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w; x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    }
+    __device__ __forceinline__ static void load(const float* p, float* x) { convert(load_raw(p), x); }
     __device__ __forceinline__ static void store(float* p, const float* x) {
         reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
         reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
@@ -96,20 +102,10 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
             }
         }
     };
-    fill(tb);
-    for (int64_t t = tb; t < te; ++t) {
-        if (t >= s1) {  // crossed into the next non-empty sequence
-            while (seq_start(a.cu, a.T, n + 1) <= t) ++n;
-            s0 = seq_start(a.cu, a.T, n);
-            s1 = seq_start(a.cu, a.T, n + 1);
-            fill(t);
-        }
-        float cur[8], out[8];
-        if (live) V8<T>::load(x + t * a.C + c0, cur);
-        else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cur[e] = 0.f;
-        }
+    // one token: convolution over the window and the current input, Swish, optional L2Norm,
+    // store, then slide the window
+    auto token = [&](int64_t t, const float* cur) __attribute__((always_inline)) {
+        float out[8];
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -134,6 +130,49 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) win[HIST > 0 ? HIST - 1 : 0][e] = cur[e];
         }
+    };
+    if (te <= s1 && te - tb == kSegT && tb - HIST >= s0 && live) {
+        // the common case, a whole segment inside one sequence with its history: every load is
+        // issued ahead of its use -- the history rows together, then each group of kU tokens
+        // while the previous group is computed -- so each lane keeps up to 2 kU loads in flight
+        constexpr int kU = 8, kG = kSegT / kU;
+        typename V8<T>::Raw hist[HIST > 0 ? HIST : 1], raw[2][kU];
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) hist[i] = V8<T>::load_raw(x + (tb - HIST + i) * a.C + c0);
+        auto issue = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) raw[gi & 1][u] = V8<T>::load_raw(x + (tb + gi * kU + u) * a.C + c0);
+        };
+        issue(0);
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) V8<T>::convert(hist[i], win[i]);
+#pragma unroll
+        for (int gi = 0; gi < kG; ++gi) {
+            if (gi + 1 < kG) issue(gi + 1);
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                float cur[8];
+                V8<T>::convert(raw[gi & 1][u], cur);
+                token(tb + gi * kU + u, cur);
+            }
+        }
+        return;
+    }
+    fill(tb);
+    for (int64_t t = tb; t < te; ++t) {
+        if (t >= s1) {  // crossed into the next non-empty sequence
+            while (seq_start(a.cu, a.T, n + 1) <= t) ++n;
+            s0 = seq_start(a.cu, a.T, n);
+            s1 = seq_start(a.cu, a.T, n + 1);
+            fill(t);
+        }
+        float cur[8];
+        if (live) V8<T>::load(x + t * a.C + c0, cur);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cur[e] = 0.f;
+        }
+        token(t, cur);
     }
 }
 
