@@ -68,11 +68,21 @@ def test_prefill_stress_gates(z_mean):
 
 
 def test_prefill_eight_wave_path():
-    """More (sequence, head) chains than half the compute units selects one state-pass
-    workgroup covering all 128 dv columns (two 16-column tiles per compute wave)."""
+    """256 (sequence, head) chains: the state pass uses 64-column slices (four compute waves
+    and four loader waves per workgroup)."""
     inp = workloads.prefill_inputs([80] * 16, H=16, dk=128, dv=128, dtype="bf16", seed=12,
                                    s0_std=0.02, name="n16_h16_t80")
     _check_prefill(inp, use_cu=False)
+
+
+@pytest.mark.parametrize("n,H,dtype", [(3, 16, "bf16"), (3, 16, "fp32"), (5, 16, "fp32"), (2, 16, "fp32")])
+def test_prefill_state_pass_shapes(n, H, dtype):
+    """The state-pass slice width follows the number of (sequence, head) chains on a 256-CU
+    device: 48 chains take 32-column slices, 80 take 64-column slices, 32 take 16-column
+    slices (fp32 at d = 128: the single-role kernel, which holds fp32 v rows)."""
+    inp = workloads.prefill_inputs([70 + 31 * i for i in range(n)], H=H, dk=128, dv=128, dtype=dtype,
+                                   seed=18 + n, s0_std=0.02, name=f"shape_n{n}_h{H}_{dtype}")
+    _check_prefill(inp)
 
 
 def test_prefill_fp32_d128_and_bf16_d64():
