@@ -50,11 +50,16 @@ def decode_bytes_per_pair(dk: int, dv: int, elem: int):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so a stored counter
+    summary stays valid across comment edits and is dropped by any code change."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_sequence_chunkwise_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

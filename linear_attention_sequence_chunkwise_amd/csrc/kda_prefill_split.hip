@@ -619,8 +619,8 @@ __device__ __forceinline__ bool chain_pos(const SplitArgs& a, ChainPos& p) {
 // not through registers), piece p by wave p mod NLW; block pieces below Block::NQP (Q~, M) go
 // to one destination, the rest (K~, K^n, T, e^{Gamma_n}) to another.  With each chunk's copies
 // they also pull the next chunk's block lines (this slice's share, line slice + nslices m) and
-// v rows into L2 with loads whose results are only folded into a sink at the next fetch, so
-// nothing waits for them: the copies then find their lines in L2 instead of waiting on the
+// v rows into L2, with 4-byte LDS-DMA loads into a dummy area that nothing reads, so nothing
+// waits for them: the next copies then find their lines in L2 instead of waiting on the
 // farther memory with only one chunk of look-ahead.
 template <int DK, int DVS, typename TIn, int NLW, int TL = 1>
 struct StageLoader {
