@@ -25,8 +25,9 @@
 //   S' = diag(e^{Gamma_n}) S + (K e^{Gamma_n - Gamma})^T U,  K~ = K e^{Gamma}, Q~ = Q e^{Gamma}
 // Decayed products are factored per 16-token tile around rho_a (Gamma just before tile a):
 // row operands carry e^{Gamma_i - rho_a} in [e^-80, 1], column operands e^{rho_a - Gamma_j},
-// <= 1 off the diagonal and < e^80 on it -- the pages' bound.  Decays are cumulative
-// products of alpha = e^g, never exponentials of large sums.
+// <= 1 off the diagonal and < e^80 on it -- the pages' bound.  Within a tile a decay is the
+// exponential of a sum of at most 16 log-decays (bounded by the same -80); across tiles,
+// decays are products of tile totals, never exponentials of chunk-long sums.
 //
 // Factor block of one (chunk, head), bf16 unless noted (offsets in the kernels below):
 //   Kt = K~ and Qt = Q~ [64 x DK], KnT = (K e^{Gamma_n - Gamma})^T [DK x 64], each stored as
@@ -205,11 +206,10 @@ struct IntraSmem {
     float beta[kC];
 };
 
-// x[lane - n] within the lane's row of 16, or 1 for the first n lanes of the row.
+// x[lane - n] within the lane's row of 16, or 0 for the first n lanes of the row.
 template <int N>
-__device__ __forceinline__ float row_shr_or_one(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x110 | N, 0xf, 0xf,
-                                                      false));
+__device__ __forceinline__ float row_shr_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
@@ -288,8 +288,10 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
     }
     lds_barrier();
 
-    // ---- gates alpha = e^g (tokens past the end: alpha = 1), then F = e^{Gamma_i - rho_w}:
-    // an inclusive product scan over the 16 tokens of the tile (lanes li of one row) ---------
+    // ---- gates, then F = e^{Gamma_i - rho_w}: log2 alpha = g log2(e) (tokens past the end: 0),
+    // an inclusive sum over the 16 tokens of the tile (lanes li of one row; a lane with no
+    // source adds 0), then one exp2.  The tile-local sum lies in [-80 log2(e), 0], the
+    // pages' 16-token bound, so the exponential is finite and normal in fp32. ----------------
     float F[KS][8];
     {
         const bool valid = r < clen;
@@ -301,25 +303,25 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float sg = fast_rcp(1.f + fast_exp2(ae8[e] * lane8(pz[s][0], pz[s][1], e)));
-                F[s][e] = valid ? fast_exp2(gscale * sg) : 1.f;
+                F[s][e] = valid ? gscale * sg : 0.f;
             }
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<1>(F[s][e]);
+            for (int e = 0; e < 8; ++e) F[s][e] += row_shr_or_zero<1>(F[s][e]);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<2>(F[s][e]);
+            for (int e = 0; e < 8; ++e) F[s][e] += row_shr_or_zero<2>(F[s][e]);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<4>(F[s][e]);
+            for (int e = 0; e < 8; ++e) F[s][e] += row_shr_or_zero<4>(F[s][e]);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) F[s][e] *= row_shr_or_one<8>(F[s][e]);
+            for (int e = 0; e < 8; ++e) F[s][e] = fast_exp2(F[s][e] + row_shr_or_zero<8>(F[s][e]));
         if (li == 15) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
