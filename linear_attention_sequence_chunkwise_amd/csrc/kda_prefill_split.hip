@@ -61,24 +61,11 @@ struct Block {
 
 __device__ __forceinline__ int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
 
-// Byte offset of element (row r, channel ch) of K~ or Q~ inside its lane-order image: piece
-// (a, s) = (r / 16, ch / 32) holds, for lane (g, li), the eight channels 32s + 8g .. of row
-// 16a + li -- exactly the 16 bytes that lane feeds to a 16x16x32 MFMA.
-template <int DK>
-__device__ __forceinline__ uint32_t lane_off(int r, int ch) {
-    return static_cast<uint32_t>((((r >> 4) * (DK / 32) + (ch >> 5)) * 64 + ((ch >> 3) & 3) * 16 + (r & 15)) * 16 +
-                                 (ch & 7) * 2);
-}
-
-// Byte offset of the four tokens t4 .. t4 + 3 (t4 a multiple of 4) of channel c in the
-// lane-order image of K^n^T.  The state-update product uses state row tile m with rows
-// pi(m, i) = 32 (m / 2) + 8 (i / 4) + 4 (m % 2) + i % 4; piece (m, sp) holds for lane (g, li)
-// the tokens 32sp + 4g .. and 32sp + 16 + 4g .. of channel pi(m, li).
-__device__ __forceinline__ uint32_t kn_off(int c, int t4) {
-    const int m = 2 * (c >> 5) + ((c >> 2) & 1), li = 4 * ((c >> 3) & 3) + (c & 3);
-    const int u = t4 & 31;
-    return static_cast<uint32_t>(((m * 2 + (t4 >> 5)) * 64 + ((u & 15) >> 2) * 16 + li) * 16 + (u >> 4) * 8);
-}
+// Lane-order images in a factor block.  K~ and Q~: 1 KiB piece (a, s), a = row tile, s = 32-
+// channel step, holds for lane (g, li) the eight channels 32s + 8g .. of row 16a + li -- the 16
+// bytes that lane feeds to a 16x16x32 MFMA.  K^n^T: piece (m, sp) holds for lane (g, li) the
+// tokens 32sp + 4g .. + 3 and 32sp + 16 + 4g .. + 3 of channel pi(m, li), with the state row
+// order pi(m, i) = 32 (m / 2) + 8 (i / 4) + 4 (m % 2) + i % 4 of the state-update product.
 
 __device__ __forceinline__ uint4 scale8(uint4 x, float4 s0, float4 s1) {
     return make_uint4(pack_bf16x2(lo_bf16(x.x) * s0.x, hi_bf16(x.x) * s0.y),
