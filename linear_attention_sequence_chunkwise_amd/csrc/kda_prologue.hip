@@ -53,6 +53,12 @@ template <> struct V8<float> {
     }
 };
 
+// x of another lane of the same row of 16, chosen by a DPP control code
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 // sequence containing packed token t (the last sequence whose start is <= t)
 __device__ __forceinline__ int seq_of(const int32_t* cu, int n_seqs, int64_t T, int64_t t) {
     if (!cu) return static_cast<int>(t / T);
@@ -65,7 +71,8 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int n_seqs, int64_t T, 
 }
 }  // namespace
 
-template <int W, typename T>
+// L2 = a.l2 (0, 64 or 128) as a constant, so the per-head sum is an unrolled butterfly
+template <int W, int L2, typename T>
 __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
     constexpr int HIST = W - 1;
     const int c0 = blockIdx.y * kChanPerBlock + threadIdx.x * 8;
@@ -104,7 +111,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
     };
     // one token: convolution over the window and the current input, Swish, optional L2Norm,
     // store, then slide the window
-    auto token = [&](int64_t t, const float* cur) __attribute__((always_inline)) {
+    auto token = [&](int64_t t, const float* cur, bool store) __attribute__((always_inline)) {
         float out[8];
         float ss = 0.f;
 #pragma unroll
@@ -115,13 +122,19 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
             out[e] = acc * fast_rcp(1.f + fast_exp2(-acc * kLog2e));  // Swish
             ss += out[e] * out[e];
         }
-        if (a.l2 > 0) {
-            for (int off = 1; off < a.l2 / 8; off <<= 1) ss += __shfl_xor(ss, off);
+        if constexpr (L2 > 0) {
+            // sum over the L2 / 8 lanes of one head with DPP lane permutations (no LDS trips):
+            // quads, then the two quads of each half row (mirror), then the two half rows
+            static_assert(L2 == 64 || L2 == 128, "L2Norm over 64 or 128 channels");
+            ss += dpp_f32<0xB1>(ss);   // quad_perm [1,0,3,2]
+            ss += dpp_f32<0x4E>(ss);   // quad_perm [2,3,0,1]
+            ss += dpp_f32<0x141>(ss);  // row_half_mirror
+            if constexpr (L2 == 128) ss += dpp_f32<0x128>(ss);  // row_ror:8
             const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
-        if (live) V8<T>::store(y + t * a.C + c0, out);
+        if (store) V8<T>::store(y + t * a.C + c0, out);
 #pragma unroll
         for (int i = 0; i + 1 < HIST; ++i)
 #pragma unroll
@@ -153,7 +166,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
             for (int u = 0; u < kU; ++u) {
                 float cur[8];
                 V8<T>::convert(raw[gi & 1][u], cur);
-                token(tb + gi * kU + u, cur);
+                token(tb + gi * kU + u, cur, true);  // every lane here is live
             }
         }
         return;
@@ -172,7 +185,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) cur[e] = 0.f;
         }
-        token(t, cur);
+        token(t, cur, live);
     }
 }
 
@@ -195,17 +208,24 @@ __global__ void __launch_bounds__(256) conv_cache_kernel(ShortConvArgs a) {
     for (int j = 0; j < hist; ++j) a.cache_out[idx * hist + j] = v[j];
 }
 
+template <int L2, typename T>
+static void launch_conv_w(const ShortConvArgs& a, dim3 grid, hipStream_t stream) {
+    switch (a.W) {
+        case 1: hipLaunchKernelGGL((short_conv_kernel<1, L2, T>), grid, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((short_conv_kernel<2, L2, T>), grid, dim3(256), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((short_conv_kernel<3, L2, T>), grid, dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((short_conv_kernel<4, L2, T>), grid, dim3(256), 0, stream, a); break;
+    }
+}
+
 template <typename T>
 static hipError_t launch_conv_t(const ShortConvArgs& a, hipStream_t stream) {
     if (a.total > 0) {
         const dim3 grid(static_cast<unsigned>((a.total + kSegT - 1) / kSegT),
                         static_cast<unsigned>((a.C + kChanPerBlock - 1) / kChanPerBlock));
-        switch (a.W) {
-            case 1: hipLaunchKernelGGL((short_conv_kernel<1, T>), grid, dim3(256), 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((short_conv_kernel<2, T>), grid, dim3(256), 0, stream, a); break;
-            case 3: hipLaunchKernelGGL((short_conv_kernel<3, T>), grid, dim3(256), 0, stream, a); break;
-            default: hipLaunchKernelGGL((short_conv_kernel<4, T>), grid, dim3(256), 0, stream, a); break;
-        }
+        if (a.l2 == 128) launch_conv_w<128, T>(a, grid, stream);
+        else if (a.l2 == 64) launch_conv_w<64, T>(a, grid, stream);
+        else launch_conv_w<0, T>(a, grid, stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
