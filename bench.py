@@ -248,6 +248,7 @@ def main():
         out["spec_decode"] = bench_spec_decode()
         out["output_gate"] = bench_output_gate()
         out["short_conv"] = bench_short_conv()
+        out["gate"] = bench_gate()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
@@ -409,6 +410,37 @@ def bench_short_conv(repeats: int = 10):
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                          "kernel": "short_conv_kernel", "algorithmic_bytes_per_launch": byts}}
+
+
+def bench_gate(repeats: int = 10):
+    """Standalone gate g = g_min*Sigmoid(e^A z) with its chunk-local cumulative sum, over the
+    batched prefill workload's z: 4 x 32768 tokens x 32 heads x 128 channels, fp32 in, g and
+    gcum fp32 out: 3 x 2.15 GB moved."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda
+    N, T, H, dk = 4, 32768, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(11)
+    z = torch.randn(N * T, H, dk, device="cuda", generator=g)
+    A = torch.randn(H, dk, device="cuda", generator=g) * 0.5
+    gv, gc = torch.empty_like(z), torch.empty_like(z)
+    run = lambda: kda.kda_gate(z, A, g=gv, gcum=gc, n_seqs=N)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(repeats):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / repeats
+    byts = 3 * z.numel() * 4 + A.numel() * 4
+    gbps = byts / t / 1e9
+    del z, gv, gc
+    return {"workload": "gate_b4_t32768_h32_d128_f32", "us_per_call": t * 1e6,
+            "hbm_GBps": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "gate_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
 if __name__ == "__main__":

@@ -63,9 +63,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
         const int64_t e = s + a.chunk < e_n ? s + a.chunk : e_n;
         if (active) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int64_t t = s; t < e; ++t) {
-                const int64_t idx = t * ncol4 + col;
-                const float4 z = z4[idx];
+            auto token = [&](int64_t idx, float4 z) __attribute__((always_inline)) {
                 float4 gv;
                 gv.x = gm * fast_rcp(1.f + fast_exp2(ae.x * z.x));
                 gv.y = gm * fast_rcp(1.f + fast_exp2(ae.y * z.y));
@@ -74,7 +72,31 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                 acc.x += gv.x; acc.y += gv.y; acc.z += gv.z; acc.w += gv.w;
                 if (g4) g4[idx] = gv;
                 if (c4) c4[idx] = acc;
+            };
+            constexpr int kU = 8;
+            int64_t t = s;
+            if ((e - s) % kU == 0) {
+                // whole groups of kU tokens: each group's inputs are loaded while the previous
+                // group is computed, so a thread keeps up to 2 kU loads in flight
+                float4 zb[2][kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) zb[0][u] = z4[(s + u) * ncol4 + col];
+                for (int gi = 0; s + gi * kU < e; gi += 2) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int64_t tg = s + (gi + h2) * kU;
+                        if (tg >= e) break;
+                        if (tg + kU < e) {
+#pragma unroll
+                            for (int u = 0; u < kU; ++u) zb[h2 ^ 1][u] = z4[(tg + kU + u) * ncol4 + col];
+                        }
+#pragma unroll
+                        for (int u = 0; u < kU; ++u) token((tg + u) * ncol4 + col, zb[h2][u]);
+                    }
+                }
+                t = e;
             }
+            for (; t < e; ++t) token(t * ncol4 + col, z4[t * ncol4 + col]);
         }
         s = e;
     }
