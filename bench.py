@@ -6,8 +6,9 @@
 A step is one kda_prefill_fwd call over the named prefill workload (gate, intra-chunk
 products, triangular solve, state pass and outputs all run inside it).  The same line also
 carries the decode half of the metric: 256 consecutive kda_decode_step calls over
-512 sequences x 32 heads.  Inputs are seeded synthetic data resident in HBM before timing.
-Prints one JSON line.
+512 sequences x 32 heads, a speculative-decode round, and standalone timings of the output
+epilogue, the input prologue and the gate at the batched workload's sizes.  Inputs are seeded
+synthetic data resident in HBM before timing.  Prints one JSON line.
 """
 from __future__ import annotations
 
