@@ -79,6 +79,26 @@ def read_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
+def read_mfma(workload: str):
+    """Executed MFMA work of one prefill call from rocprofv3 counters, if a summary for the
+    current kernel sources exists under profiles/ (else None): bf16 MFMA flops executed
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, including masked tiles and per-slice recompute) and
+    the fraction of SIMD cycles the MFMA units were busy over the call's kernels
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_mfma.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    m_fl = re.search(r"executed_bf16_flops_per_launch:\s*([0-9.eE+]+)", txt)
+    m_busy = re.search(r"mfma_busy_frac_per_launch:\s*([0-9.eE+-]+)", txt)
+    if not m_hash or not m_fl or not m_busy or m_hash.group(1) != kernel_source_hash():
+        return None
+    return {"executed_bf16_flops_per_launch": float(m_fl.group(1)),
+            "mfma_busy_frac": float(m_busy.group(1)),
+            "source": f"profiles/{workload}_mfma.txt"}
+
+
 def cpu_threads() -> int:
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
@@ -101,9 +121,10 @@ def cpu_baseline(inp, budget_s: float = 20.0):
     _run_oracle_pairs(orc, inp, pairs[:1], 1)
     one = time.perf_counter() - t0
     per_round = max(one, 1e-4)
-    n_more = int(min(len(pairs) - 1, max(threads, (budget_s / per_round) * threads)))
-    n_more = max(0, (n_more // threads) * threads) if n_more >= threads else n_more
-    sample = pairs[1:1 + n_more] if n_more > 0 else pairs[:1]
+    n = int(min(len(pairs), max(threads, (budget_s / per_round) * threads)))
+    if n < len(pairs):
+        n = max(1, (n // threads) * threads)
+    sample = pairs[:n]   # the whole workload when it fits the budget
     t0 = time.perf_counter()
     _run_oracle_pairs(orc, inp, sample, threads)
     secs = time.perf_counter() - t0
@@ -115,17 +136,22 @@ def cpu_baseline(inp, budget_s: float = 20.0):
 
 
 def _run_oracle_pairs(orc, inp, pairs, threads):
+    """Runs the oracle on the given (sequence, head) pairs.  Heads are passed in contiguous
+    batches of bounded host memory, so every batch offers all its pairs to the threads."""
     f = lambda t: t.float().numpy()
-    # pass only the needed heads' data via per-pair slices to keep host memory bounded
-    by_head = {}
-    for n, h in pairs:
-        by_head.setdefault(h, []).append(n)
-    for h, ns in by_head.items():
-        sl = slice(h, h + 1)
+    per_head = inp.total * inp.dk
+    hb = max(1, min(inp.H, (1 << 26) // max(per_head, 1)))
+    wanted = set(pairs)
+    for h0 in range(0, inp.H, hb):
+        h1 = min(inp.H, h0 + hb)
+        sub = [(n, h - h0) for n, h in pairs if h0 <= h < h1 and (n, h) in wanted]
+        if not sub:
+            continue
+        sl = slice(h0, h1)
         orc.prefill(f(inp.q[:, sl]), f(inp.k[:, sl]), f(inp.v[:, sl]), f(inp.beta[:, sl]),
                     z=inp.z[:, sl].numpy(), A=inp.A[sl].numpy(),
                     S0=None if inp.S0 is None else inp.S0[:, sl].numpy(),
-                    cu_seqlens=inp.cu_seqlens.numpy(), pairs=[(n, 0) for n in ns],
+                    cu_seqlens=inp.cu_seqlens.numpy(), pairs=sub,
                     n_threads=threads, want_state=False)
 
 
@@ -243,6 +269,11 @@ def main():
                       "frac": mfma_tflops / BF16_PEAK_TFLOPS,
                       "useful_flops_per_token_head": fl},
     }
+
+    mf = read_mfma(name)
+    if mf is not None:
+        mf["executed_tflops"] = mf["executed_bf16_flops_per_launch"] / (ms_event * 1e-3) / 1e12
+    out["mfma_util"]["rocprof"] = mf
 
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps)

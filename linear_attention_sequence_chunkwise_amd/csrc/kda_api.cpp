@@ -112,6 +112,8 @@ kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* 
     if (!cu_seqlens && n_seqs > 0 && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
     if (total > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
     if (static_cast<int64_t>(n_seqs) * H > int64_t(0x7fffffff) / 16 || H > 65535) return KDA_ERR_SHAPE;
+    // one intra-chunk workgroup per (chunk slot, head) in a 1-D grid
+    if (kda::split_max_chunks(total, n_seqs) > int64_t(0x7fffffff) / H) return KDA_ERR_SHAPE;
     // 64 token rows of one chunk must span < 2^31 bytes (32-bit buffer offsets)
     if (static_cast<int64_t>(H) * dk * 4 * 64 >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !beta_aligned(beta, dt) ||

@@ -94,6 +94,26 @@ __device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// Streaming 16-byte global accesses for data that one kernel touches exactly once (inputs
+// read once, outputs written once): the nontemporal hint keeps them from displacing lines
+// that other accesses reuse.
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, static_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ float4 ld_stream_f4(const void* p) {
+    const uint4 u = ld_stream16(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+}
+__device__ __forceinline__ void st_stream_f4(void* p, float4 v) {
+    st_stream16(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                              __float_as_uint(v.w)));
+}
+
 // LDS-DMA: the 64 lanes' 16-byte pieces at byte offsets voff of r are written, in lane
 // order, to the contiguous 1 KiB at lds (a workgroup-uniform LDS address), without passing
 // through registers.  Out-of-range lanes write zeros.  Completion is tracked by vmcnt.

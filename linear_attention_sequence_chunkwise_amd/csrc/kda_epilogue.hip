@@ -21,24 +21,24 @@ namespace {
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16_t> {
     __device__ __forceinline__ static void load(const bf16_t* p, float* x) {
-        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint4 u = ld_stream16(p);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) { x[2 * i] = lo_bf16(w[i]); x[2 * i + 1] = hi_bf16(w[i]); }
     }
     __device__ __forceinline__ static void store(bf16_t* p, const float* x) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+        st_stream16(p, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
     }
 };
 template <> struct Vec8<float> {
     __device__ __forceinline__ static void load(const float* p, float* x) {
-        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+        const float4 a = ld_stream_f4(p), b = ld_stream_f4(p + 4);
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }
     __device__ __forceinline__ static void store(float* p, const float* x) {
-        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        st_stream_f4(p, make_float4(x[0], x[1], x[2], x[3]));
+        st_stream_f4(p + 4, make_float4(x[4], x[5], x[6], x[7]));
     }
 };
 

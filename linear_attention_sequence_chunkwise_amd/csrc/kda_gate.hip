@@ -70,8 +70,8 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                 gv.z = gm * fast_rcp(1.f + fast_exp2(ae.z * z.z));
                 gv.w = gm * fast_rcp(1.f + fast_exp2(ae.w * z.w));
                 acc.x += gv.x; acc.y += gv.y; acc.z += gv.z; acc.w += gv.w;
-                if (g4) g4[idx] = gv;
-                if (c4) c4[idx] = acc;
+                if (g4) st_stream_f4(g4 + idx, gv);
+                if (c4) st_stream_f4(c4 + idx, acc);
             };
             constexpr int kU = 8;
             int64_t t = s;
@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                 // group is computed, so a thread keeps up to 2 kU loads in flight
                 float4 zb[2][kU];
 #pragma unroll
-                for (int u = 0; u < kU; ++u) zb[0][u] = z4[(s + u) * ncol4 + col];
+                for (int u = 0; u < kU; ++u) zb[0][u] = ld_stream_f4(z4 + (s + u) * ncol4 + col);
                 for (int gi = 0; s + gi * kU < e; gi += 2) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                         if (tg >= e) break;
                         if (tg + kU < e) {
 #pragma unroll
-                            for (int u = 0; u < kU; ++u) zb[h2 ^ 1][u] = z4[(tg + kU + u) * ncol4 + col];
+                            for (int u = 0; u < kU; ++u) zb[h2 ^ 1][u] = ld_stream_f4(z4 + (tg + kU + u) * ncol4 + col);
                         }
 #pragma unroll
                         for (int u = 0; u < kU; ++u) token((tg + u) * ncol4 + col, zb[h2][u]);
@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                 }
                 t = e;
             }
-            for (; t < e; ++t) token(t * ncol4 + col, z4[t * ncol4 + col]);
+            for (; t < e; ++t) token(t * ncol4 + col, ld_stream_f4(z4 + t * ncol4 + col));
         }
         s = e;
     }

@@ -220,8 +220,10 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
 
+    // workgroup -> (chunk slot, head), the head fastest: the workgroups in flight together
+    // read the same tokens' rows of every head, which lie next to each other in memory
+    const int H = args.H, slot = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
     // chunk slot -> (sequence, chunk of the sequence)
-    const int slot = blockIdx.x, h = blockIdx.y, H = args.H;
     int n;
     int64_t tok0, len, c0;
     if (args.cu) {
@@ -1194,7 +1196,7 @@ static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
     const int64_t slots = a.cu ? split_max_chunks(a.total, a.n_seqs)
                                : static_cast<int64_t>(a.n_seqs) * ((a.T + kC - 1) / kC);
     if (slots > 0) {
-        hipLaunchKernelGGL((prefill_intra_kernel<DK, TIn>), dim3(static_cast<unsigned>(slots), a.H), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_intra_kernel<DK, TIn>), dim3(static_cast<unsigned>(slots * a.H)), dim3(256), 0,
                            stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -26,7 +26,7 @@ constexpr int kChanPerBlock = 2048;  // 256 threads x 8 channels
 template <typename T> struct V8;
 template <> struct V8<bf16_t> {
     struct Raw { uint4 a; };  // eight channels as loaded, converted later (a use would wait)
-    __device__ __forceinline__ static Raw load_raw(const bf16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
+    __device__ __forceinline__ static Raw load_raw(const bf16_t* p) { return Raw{ld_stream16(p)}; }
     __device__ __forceinline__ static void convert(const Raw& r, float* x) {
         const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
@@ -34,22 +34,22 @@ template <> struct V8<bf16_t> {
     }
     __device__ __forceinline__ static void load(const bf16_t* p, float* x) { convert(load_raw(p), x); }
     __device__ __forceinline__ static void store(bf16_t* p, const float* x) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+        st_stream16(p, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
     }
 };
 template <> struct V8<float> {
     struct Raw { float4 a, b; };
     __device__ __forceinline__ static Raw load_raw(const float* p) {
-        return Raw{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+        return Raw{ld_stream_f4(p), ld_stream_f4(p + 4)};
     }
     __device__ __forceinline__ static void convert(const Raw& r, float* x) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w; x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
     __device__ __forceinline__ static void load(const float* p, float* x) { convert(load_raw(p), x); }
     __device__ __forceinline__ static void store(float* p, const float* x) {
-        reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-        reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        st_stream_f4(p, make_float4(x[0], x[1], x[2], x[3]));
+        st_stream_f4(p + 4, make_float4(x[4], x[5], x[6], x[7]));
     }
 };
 

@@ -73,6 +73,8 @@ def test_prefill_rejects_bad_arguments(lib):
     # a final state that partially overlaps the initial state
     assert prefill(lib, s0=ctypes.c_void_p(0x100000), sN=ctypes.c_void_p(0x100010)) == ESHAPE
     assert prefill(lib, T=1 << 45, N=1 << 10) == ESHAPE
+    # (chunk slots) x heads intra-chunk workgroups must fit one 1-D grid
+    assert prefill(lib, H=65535, T=64 * 40000) == ESHAPE
 
 
 def test_checkpointed_prefill_rejects_bad_arguments(lib):
