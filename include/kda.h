@@ -123,6 +123,9 @@ size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int d
  *   workspace      device scratch of at least kda_prefill_workspace_size(...) bytes,
  *                  16-byte aligned (KDA_ERR_WORKSPACE otherwise); may be NULL only when
  *                  there is nothing to compute; contents on return are undefined
+ * Size limits (KDA_ERR_SHAPE beyond them): H <= 65535; 64 token rows of one head's z span
+ * less than 2^31 bytes (H * dk * 256 < 2^31); (ceil(total / 64) + N) * H <= 2^31 - 1, one
+ * intra-chunk workgroup per (chunk, head).
  * A zero-length sequence writes no output rows and copies its initial state (or zeros) to
  * final_state.  Results equal the token recurrence up to floating-point association.
  */
