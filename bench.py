@@ -173,9 +173,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one MI355X: this build runs on a single GPU "
-              "(the (sequence, head) chains shard across GPUs with no communication; "
-              "multi-GPU runs are not part of it).", file=sys.stderr)
+        print("bench.py measures one MI355X only; --gpus above 1 is not supported "
+              "(the (sequence, head) chains would shard across GPUs with no communication, "
+              "and each GPU would run this single-GPU path on its share).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -374,7 +374,8 @@ def bench_spec_decode(K: int = 4, rounds: int = 32, repeats: int = 3):
     return {"workload": "spec_decode_n512_h32_d128_bf16_k%d" % K, "draft_tokens": K,
             "us_per_round": t * 1e6, "tokens_per_s": d.N * K / t, "hbm_GBps": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic("spec_decode_n512_h32_d128_bf16_k%d" % K),
                          "kernel": "decode_multi_kernel (verify + commit)",
                          "algorithmic_bytes_per_launch": byts},
             "inputs": "8 distinct seeded rounds cycled; full acceptance"}
@@ -406,7 +407,8 @@ def bench_output_gate(repeats: int = 10):
     return {"workload": "output_gate_rows4194304_dv128_bf16", "us_per_call": t * 1e6,
             "hbm_GBps": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic("output_gate_rows4194304_dv128_bf16"),
                          "kernel": "output_gate_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
@@ -440,7 +442,8 @@ def bench_short_conv(repeats: int = 10):
     return {"workload": "short_conv_b4_t32768_c4096_w4_bf16", "us_per_call": t * 1e6,
             "hbm_GBps": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic("short_conv_b4_t32768_c4096_w4_bf16"),
                          "kernel": "short_conv_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
@@ -471,7 +474,8 @@ def bench_gate(repeats: int = 10):
     return {"workload": "gate_b4_t32768_h32_d128_f32", "us_per_call": t * 1e6,
             "hbm_GBps": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic("gate_b4_t32768_h32_d128_f32"),
                          "kernel": "gate_kernel", "algorithmic_bytes_per_launch": byts}}
 
 
