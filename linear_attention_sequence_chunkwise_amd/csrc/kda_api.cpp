@@ -68,6 +68,10 @@ kda_status kda_gate(const float* z, const float* A, float* g, float* gcum, int64
     if (total_tokens > kMaxElems / (static_cast<int64_t>(H) * dk)) return KDA_ERR_SHAPE;
     if (static_cast<int64_t>(H) * dk / 4 > int64_t(65535) * 256) return KDA_ERR_SHAPE;
     if ((total_tokens + chunk - 1) / chunk > int64_t(0x7fffffff)) return KDA_ERR_SHAPE;
+    // one workgroup of 256 threads per (token window, 1024-channel block) in a 1-D grid
+    if ((total_tokens + chunk - 1) / chunk * ((static_cast<int64_t>(H) * dk / 4 + 255) / 256) >
+        int64_t(0xffffffff) / 256)
+        return KDA_ERR_SHAPE;
     if (!aligned16(z) || !aligned16(A) || (g && !aligned16(g)) || (gcum && !aligned16(gcum)) ||
         (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)))
         return KDA_ERR_ALIGN;
@@ -283,6 +287,8 @@ kda_status kda_short_conv(kda_dtype dt, const void* x, const float* weight, int 
     if (!cu_seqlens && T_or_total > kMaxElems / n_seqs) return KDA_ERR_SHAPE;
     const int64_t total = cu_seqlens ? T_or_total : static_cast<int64_t>(n_seqs) * T_or_total;
     if (total > kMaxElems / C) return KDA_ERR_SHAPE;
+    // one workgroup of 256 threads per (64-token segment, 2048-channel block) in a 1-D grid
+    if ((total + 63) / 64 * ((C + 2047) / 2048) > int64_t(0xffffffff) / 256) return KDA_ERR_SHAPE;
     if (!weight || (total > 0 && (!x || !y))) return KDA_ERR_NULL;
     if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(weight) & 3u) ||
         (reinterpret_cast<uintptr_t>(cache_in) & 3u) || (reinterpret_cast<uintptr_t>(cache_out) & 3u) ||

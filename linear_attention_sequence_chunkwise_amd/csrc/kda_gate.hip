@@ -30,9 +30,12 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int64_t T, int n_seqs
 
 __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
     const int64_t ncol4 = static_cast<int64_t>(a.H) * a.dk / 4;
-    const int64_t col = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x;
+    // workgroup -> (token window, column block) with the column block fastest: the
+    // workgroups in flight together cover whole token rows
+    const unsigned ncb = static_cast<unsigned>((ncol4 + 255) / 256);
+    const int64_t col = static_cast<int64_t>(blockIdx.x % ncb) * 256 + threadIdx.x;
     const bool active = col < ncol4;
-    const int64_t w_lo = static_cast<int64_t>(blockIdx.x) * a.chunk;
+    const int64_t w_lo = static_cast<int64_t>(blockIdx.x / ncb) * a.chunk;
     const int64_t w_hi = w_lo + a.chunk < a.total ? w_lo + a.chunk : a.total;
     if (w_lo >= a.total) return;
 
@@ -105,7 +108,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
     const int64_t windows = (a.total + a.chunk - 1) / a.chunk;
     const int64_t ncol4 = static_cast<int64_t>(a.H) * a.dk / 4;
-    const dim3 grid(static_cast<unsigned>(windows), static_cast<unsigned>((ncol4 + 255) / 256));
+    const dim3 grid(static_cast<unsigned>(windows * ((ncol4 + 255) / 256)));
     hipLaunchKernelGGL(gate_kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -75,9 +75,14 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int n_seqs, int64_t T, 
 template <int W, int L2, typename T>
 __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
     constexpr int HIST = W - 1;
-    const int c0 = blockIdx.y * kChanPerBlock + threadIdx.x * 8;
+    // workgroup -> (segment, channel block) with the channel block fastest: the workgroups
+    // in flight together cover whole token rows
+    const int ncb = (a.C + kChanPerBlock - 1) / kChanPerBlock;
+    const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(ncb));
+    const int64_t seg = static_cast<int64_t>(blockIdx.x / static_cast<unsigned>(ncb));
+    const int c0 = cb * kChanPerBlock + threadIdx.x * 8;
     const bool live = c0 < a.C;
-    const int64_t tb = static_cast<int64_t>(blockIdx.x) * kSegT;
+    const int64_t tb = seg * kSegT;
     const int64_t te = tb + kSegT < a.total ? tb + kSegT : a.total;
     const T* x = static_cast<const T*>(a.x);
     T* y = static_cast<T*>(a.y);
@@ -221,8 +226,8 @@ static void launch_conv_w(const ShortConvArgs& a, dim3 grid, hipStream_t stream)
 template <typename T>
 static hipError_t launch_conv_t(const ShortConvArgs& a, hipStream_t stream) {
     if (a.total > 0) {
-        const dim3 grid(static_cast<unsigned>((a.total + kSegT - 1) / kSegT),
-                        static_cast<unsigned>((a.C + kChanPerBlock - 1) / kChanPerBlock));
+        const dim3 grid(static_cast<unsigned>((a.total + kSegT - 1) / kSegT *
+                                              ((a.C + kChanPerBlock - 1) / kChanPerBlock)));
         if (a.l2 == 128) launch_conv_w<128, T>(a, grid, stream);
         else if (a.l2 == 64) launch_conv_w<64, T>(a, grid, stream);
         else launch_conv_w<0, T>(a, grid, stream);

@@ -107,6 +107,8 @@ def test_gate_rejects_bad_arguments(lib):
     assert gate(T=0) == OK  # nothing to do, nothing launched
     assert gate(T=0, z=None, g=None, gc=None) == OK  # no tokens: per-token pointers unused
     assert gate(A=None) == ENULL
+    # (token windows) x (column blocks) workgroups of 256 threads must fit one grid
+    assert gate(T=1 << 25, chunk=1) == ESHAPE
 
 
 def test_decode_rejects_bad_arguments(lib):
@@ -161,6 +163,8 @@ def test_short_conv_rejects_bad_arguments(lib):
     assert sc(x=MIS) == EALIGN and sc(cu=ctypes.c_void_p(0x10002)) == EALIGN
     assert sc(y=P) == ESHAPE                      # y must not be x
     assert sc(T=0) == OK
+    # (64-token segments) x (2048-channel blocks) workgroups of 256 threads must fit one grid
+    assert sc(T=1 << 31, C=8, l2=0) == ESHAPE
 
 
 def test_workspace_size_is_aligned(lib):
