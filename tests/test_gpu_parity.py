@@ -143,15 +143,18 @@ def _gate_tol(chunk):
     return chunk * float(np.spacing(np.float32(5.0 * chunk))) / 2 + chunk * 1e-5
 
 
-@pytest.mark.parametrize("lens,chunk", [([300], 64), ([0, 5, 64, 0, 130, 1, 77], 64),
-                                        ([1000, 333], 16), ([129, 64, 65], 100)])
-def test_gate_parity(lens, chunk):
-    rng = np.random.default_rng(sum(lens) + chunk)
-    T, H, dk = int(sum(lens)), 3, 128
+# H = 11 spreads the 352 four-channel columns over two workgroup column blocks, the second
+# one partial
+@pytest.mark.parametrize("lens,chunk,H", [([300], 64, 3), ([0, 5, 64, 0, 130, 1, 77], 64, 3),
+                                          ([1000, 333], 16, 3), ([129, 64, 65], 100, 3),
+                                          ([0, 5, 64, 0, 130, 1, 77], 64, 11)])
+def test_gate_parity(lens, chunk, H):
+    rng = np.random.default_rng(sum(lens) + chunk + H)
+    T, dk = int(sum(lens)), 128
     z = rng.normal(0, 2, (T, H, dk)).astype(np.float32)
     A = rng.normal(0, 0.5, (H, dk)).astype(np.float32)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    note(f"[gate] lens={lens} chunk={chunk}")
+    note(f"[gate] lens={lens} chunk={chunk} H={H}")
     g, gc = kda.kda_gate(torch.from_numpy(z).cuda(), torch.from_numpy(A).cuda(),
                          cu_seqlens=torch.from_numpy(cu).cuda(), chunk=chunk)
     torch.cuda.synchronize()

@@ -45,9 +45,10 @@ def _check(y, co, x, w, cache, cu, l2, dtype):
     return d.max(initial=0.0)
 
 
+# C = 2304: two 2048-channel workgroup blocks, the second one partial
 @pytest.mark.parametrize("C,width,l2,dtype", [(256, 4, 128, torch.bfloat16), (192, 3, 64, torch.float32),
                                               (4096, 4, 128, torch.bfloat16), (128, 2, 0, torch.bfloat16),
-                                              (64, 1, 64, torch.float32)])
+                                              (64, 1, 64, torch.float32), (2304, 4, 128, torch.bfloat16)])
 def test_short_conv_varlen_parity(C, width, l2, dtype):
     lengths = [0, 1, 2, 3, 31, 32, 33, 100, 0, 7]
     x, w, cache, cu = _inputs(lengths, C, width, dtype, seed=100 + C + width)
