@@ -159,13 +159,13 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* cu, in
 // One workgroup of four waves per (chunk, head).  Wave w owns 16-token tile w and works in
 // the MFMA operand layout from the start: lane (g, li) holds token 16w + li and the channels
 // 32s + 8g .. 32s + 8g + 7 for every K-step s, exactly the 16 bytes per step it feeds to a
-// 16x16x32 product.  The cumulative decays within a tile are therefore an inclusive product
-// scan across the 16 lanes of a DPP row, K~ and Q~ leave registers as linear 1 KiB lane-order
-// writes, and only the column operands (read by other waves) and K^n (transposed for the
-// state pass) go through LDS.
-// Buffers whose lifetimes do not overlap share storage (36 KiB at d = 128: four workgroups
-// fit a CU's LDS): the K^n staging gives way to the tile products once it has been copied out,
-// and the column operand to T and M once the tile products have read it.
+// 16x16x32 product.  The cumulative decays within a tile are therefore an inclusive scan of
+// log-decays across the 16 lanes of a DPP row, K~ and Q~ leave registers as linear 1 KiB
+// lane-order writes, and only the column operands (read by other waves) and K^n (transposed
+// for the state pass) go through LDS.
+// Buffers whose lifetimes do not overlap share storage (39.75 KiB at d = 128: four workgroups
+// fit a CU's 160 KiB of LDS): the K^n staging gives way to the tile products once it has been
+// copied out, and the column operand to T and M once the tile products have read it.
 template <int DK>
 struct IntraSmem {
     static constexpr int KS = DK / 32;
@@ -189,6 +189,8 @@ struct IntraSmem {
         Out out;
     } b;
     float ttile[4][DK];         // e^{rho_{a+1} - rho_a}: the product of alpha over tile a
+    float pre[4][DK];           // e^{rho_w}: ttile[0] .. ttile[w-1] multiplied in order (1 for w = 0)
+    float suf[4][DK];           // e^{Gamma_n - rho_{w+1}}: ttile[w+1] .. ttile[3] in order (1 for w = 3)
     float ae[DK];               // -e^{A} log2(e)
     float beta[kC];
 };
@@ -321,6 +323,23 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
     }
     lds_barrier();
 
+    // ---- per-channel products of tile decays, once per workgroup: every wave reads its own
+    // row, so no lane selects tiles by the wave index.  e^{Gamma_n} goes to the block.
+    if (tid < DK) {
+        const float t0 = sm.ttile[0][tid], t1 = sm.ttile[1][tid], t2 = sm.ttile[2][tid], t3 = sm.ttile[3][tid];
+        const float p2 = t0 * t1, p3 = p2 * t2, s12 = t1 * t2;
+        sm.pre[0][tid] = 1.f;
+        sm.pre[1][tid] = t0;
+        sm.pre[2][tid] = p2;
+        sm.pre[3][tid] = p3;
+        sm.suf[0][tid] = s12 * t3;
+        sm.suf[1][tid] = t2 * t3;
+        sm.suf[2][tid] = t3;
+        sm.suf[3][tid] = 1.f;
+        reinterpret_cast<float*>(blk + B::DN)[tid] = p3 * t3;
+    }
+    lds_barrier();
+
     // ---- operands.  Row operands (registers): Kr = k e^{Gamma_i - rho_w}, Qr likewise.
     // Column operand (LDS): k e^{rho_{w+1} - Gamma_i}.  Factor block: K~ = k e^{Gamma_i},
     // Q~ = q e^{Gamma_i} (lane order, straight from registers), K^n staged for transposition.
@@ -332,24 +351,18 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
         uint32_t pkr[4], pqr[4], pkc[4], pkt[4], pqt[4], pkn[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            float Tt[4][4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const float4 x = *reinterpret_cast<const float4*>(&sm.ttile[a][ch + 4 * hh]);
-                Tt[a][0] = x.x; Tt[a][1] = x.y; Tt[a][2] = x.z; Tt[a][3] = x.w;
-            }
+            // e^{rho_{w+1} - rho_w}, e^{rho_w} and e^{Gamma_n - rho_{w+1}} of the four channels
+            const float4 tw4 = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4 * hh]);
+            const float4 eR4 = *reinterpret_cast<const float4*>(&sm.pre[w][ch + 4 * hh]);
+            const float4 eN4 = *reinterpret_cast<const float4*>(&sm.suf[w][ch + 4 * hh]);
+            const float tws[4] = {tw4.x, tw4.y, tw4.z, tw4.w};
+            const float eRs[4] = {eR4.x, eR4.y, eR4.z, eR4.w};
+            const float eNs[4] = {eN4.x, eN4.y, eN4.z, eN4.w};
             float vkr[4], vqr[4], vkc[4], vkt[4], vqt[4], vkn[4];
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const int e = 4 * hh + e4;
-                float tw = Tt[0][e4], eR = 1.f, eN = 1.f;
-#pragma unroll
-                for (int a = 1; a < 4; ++a) tw = w == a ? Tt[a][e4] : tw;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    eR *= a < w ? Tt[a][e4] : 1.f;
-                    eN *= a > w ? Tt[a][e4] : 1.f;
-                }
+                const float tw = tws[e4], eR = eRs[e4], eN = eNs[e4];
                 const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
                 const float f = F[s][e];
                 const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
@@ -368,11 +381,6 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
                 pkt[2 * hh + p2] = pack_bf16x2(vkt[2 * p2], vkt[2 * p2 + 1]);
                 pqt[2 * hh + p2] = pack_bf16x2(vqt[2 * p2], vqt[2 * p2 + 1]);
                 pkn[2 * hh + p2] = pack_bf16x2(vkn[2 * p2], vkn[2 * p2 + 1]);
-            }
-            if (w == 0 && li == 0) {  // e^{Gamma_n}: the product of all four tiles
-                *reinterpret_cast<float4*>(blk + B::DN + (ch + 4 * hh) * 4) =
-                    make_float4(Tt[0][0] * Tt[1][0] * Tt[2][0] * Tt[3][0], Tt[0][1] * Tt[1][1] * Tt[2][1] * Tt[3][1],
-                                Tt[0][2] * Tt[1][2] * Tt[2][2] * Tt[3][2], Tt[0][3] * Tt[1][3] * Tt[2][3] * Tt[3][3]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
