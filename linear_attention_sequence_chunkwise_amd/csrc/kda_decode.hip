@@ -240,12 +240,13 @@ __global__ void __launch_bounds__(NT) decode_multi_kernel(DecodeMultiArgs args) 
 
 // Commit uses the single-step kernel's thread tiling, so its sums run in the same order and the
 // committed state equals single steps bit for bit.  Verify, which only has to match within
-// rounding, uses half the threads: per draft token it synchronizes half as many waves.
+// rounding, uses a quarter of the threads (16 state rows per thread): per draft token it
+// synchronizes a quarter as many waves.
 template <int D, int NT, typename TIn>
 static void launch_multi_t(const DecodeMultiArgs& a, bool commit, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H));
     if (commit) hipLaunchKernelGGL((decode_multi_kernel<D, NT, TIn, true>), grid, dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((decode_multi_kernel<D, NT / 2, TIn, false>), grid, dim3(NT / 2), 0, stream, a);
+    else hipLaunchKernelGGL((decode_multi_kernel<D, NT / 4, TIn, false>), grid, dim3(NT / 4), 0, stream, a);
 }
 
 hipError_t launch_decode_multi(const DecodeMultiArgs& a, int d, bool bf16, bool commit, hipStream_t stream) {
