@@ -1,0 +1,149 @@
+"""CPU tests of the host-side logic around the kernels: the seeded input recipe, the
+roofline accounting that bench.py reports, and the readers of the rocprofv3 summaries under
+profiles/ (which must drop a summary taken for other kernel sources)."""
+from __future__ import annotations
+
+import math
+import os
+import re
+import shutil
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from linear_attention_sequence_chunkwise_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+# --- input recipe ------------------------------------------------------------------------
+
+def test_prefill_inputs_follow_the_recipe():
+    inp = workloads.prefill_inputs([70, 0, 130], H=3, dk=64, dv=32, dtype="fp32", seed=9,
+                                   s0_std=0.02)
+    assert inp.total == 200 and inp.N == 3 and inp.H == 3
+    assert inp.cu_seqlens.tolist() == [0, 70, 70, 200]
+    # q, k L2-normalised per (token, head); q then carries 1/sqrt(dk)
+    kn = np.linalg.norm(inp.k.numpy(), axis=-1)
+    qn = np.linalg.norm(inp.q.numpy(), axis=-1)
+    assert np.allclose(kn, 1.0, atol=1e-5)
+    assert np.allclose(qn, 1.0 / math.sqrt(64), atol=1e-5)
+    b = inp.beta.numpy()
+    assert b.shape == (200, 3) and np.all((b > 0) & (b < 1))
+    assert inp.z.dtype == torch.float32 and inp.A.shape == (3, 64)
+    assert inp.S0.shape == (3, 3, 64, 32) and abs(float(inp.S0.std()) - 0.02) < 2e-3
+    assert not inp.equal_length
+
+
+def test_inputs_are_reproducible_and_seed_dependent():
+    a = workloads.prefill_inputs([64], H=2, dk=64, dv=64, dtype="bf16", seed=5)
+    b = workloads.prefill_inputs([64], H=2, dk=64, dv=64, dtype="bf16", seed=5)
+    c = workloads.prefill_inputs([64], H=2, dk=64, dv=64, dtype="bf16", seed=6)
+    for x, y in [(a.q, b.q), (a.k, b.k), (a.v, b.v), (a.beta, b.beta), (a.z, b.z)]:
+        assert torch.equal(x, y)
+    assert not torch.equal(a.q, c.q)
+    assert a.q.dtype == torch.bfloat16 and a.z.dtype == torch.float32
+
+
+def test_bf16_inputs_round_the_fp32_draws_to_nearest_even():
+    f = workloads.prefill_inputs([32], H=1, dk=64, dv=64, dtype="fp32", seed=11)
+    h = workloads.prefill_inputs([32], H=1, dk=64, dv=64, dtype="bf16", seed=11)
+    assert torch.equal(f.v.to(torch.bfloat16), h.v)
+    assert torch.equal(f.z, h.z)  # the gate input stays fp32
+
+
+def test_varlen_lengths_are_log_uniform_in_range():
+    rng = np.random.default_rng(3)
+    lens = workloads.varlen_lengths(rng, 2000, 512, 16384)
+    assert min(lens) >= 512 and max(lens) <= 16384
+    logs = np.log(lens)
+    # log-uniform: the median of log L sits at the middle of [ln 512, ln 16384]
+    assert abs(np.median(logs) - 0.5 * (math.log(512) + math.log(16384))) < 0.1
+
+
+def test_decode_inputs_shapes():
+    d = workloads.decode_inputs(N=3, H=2, dk=64, dv=64, steps=5, dtype="bf16", seed=1)
+    assert d.q.shape == (5, 3, 2, 64) and d.beta.shape == (5, 3, 2)
+    assert d.S0.shape == (3, 2, 64, 64) and d.S0.dtype == torch.float32
+    assert d.steps == 5 and d.N == 3 and d.H == 2
+
+
+def test_unknown_workload_is_rejected():
+    with pytest.raises(KeyError):
+        workloads.make("no_such_workload")
+
+
+# --- roofline accounting -----------------------------------------------------------------
+
+def test_prefill_algorithmic_work_per_token_head():
+    # d = 128, chunk 64: 6 C dk dv + C(C-1) dk + 2 C(C+1) dk + 2 C(C+1) dv + C^3 / 3, per C
+    fl, by = bench.prefill_algorithmic(128, 128, 2)
+    C = 64
+    expect = (6 * C * 128 * 128 + C * (C - 1) * 128 + 2 * C * (C + 1) * 128
+              + 2 * C * (C + 1) * 128 + C ** 3 / 3) / C
+    assert fl == pytest.approx(expect) and round(fl) == 141013
+    # bf16 q, k, v, beta, o plus fp32 z
+    assert by == 3 * 128 * 2 + 2 + 4 * 128 + 128 * 2 == 1538
+    fl64, _ = bench.prefill_algorithmic(64, 64, 2)
+    assert round(fl64) == 46613
+
+
+def test_decode_bytes_per_pair():
+    # fp32 state read and written, plus one token's inputs and output
+    assert bench.decode_bytes_per_pair(128, 128, 2) == 2 * 128 * 128 * 4 + 1538 == 132610
+
+
+# --- profile summaries -------------------------------------------------------------------
+
+def test_committed_summaries_name_their_sources_and_command():
+    # a summary's figures are used only while its hash matches the kernel sources (the
+    # readers below check that); here: every summary records a hash and the command it ran
+    found = 0
+    for f in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        txt = open(os.path.join(ROOT, "profiles", f)).read()
+        assert re.search(r"kernel_source_hash:\s*[0-9a-f]{16}", txt), f"{f} names no kernel_source_hash"
+        assert "rocprofv3 " in txt and "bench.py" in txt, f"{f} gives no command"
+        found += 1
+    assert found > 0
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    csrc = os.path.join(ROOT, "linear_attention_sequence_chunkwise_amd", "csrc")
+    fake_root = tmp_path / "r"
+    dst = fake_root / "linear_attention_sequence_chunkwise_amd" / "csrc"
+    shutil.copytree(csrc, dst)
+    monkeypatch.setattr(bench, "ROOT", str(fake_root))
+    h0 = bench.kernel_source_hash()
+    f = dst / "kda_gate.hip"
+    f.write_text(f.read_text() + "\n// a new comment\n/* and a block one */\n")
+    assert bench.kernel_source_hash() == h0
+    f.write_text(f.read_text().replace("acc.x += gv.x;", "acc.x += gv.x * 1.0f;"))
+    assert bench.kernel_source_hash() != h0
+
+
+def test_summary_readers_drop_stale_summaries(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    h = bench.kernel_source_hash()
+    (prof / "w_traffic.txt").write_text(f"kernel_source_hash: {h}\ntraffic_bytes_per_launch: 1.5e+09\n")
+    (prof / "w_mfma.txt").write_text(f"kernel_source_hash: {h}\nexecuted_bf16_flops_per_launch: 2e+10\n"
+                                     "mfma_busy_frac_per_launch: 0.05\n")
+    (prof / "old_traffic.txt").write_text("kernel_source_hash: 0000000000000000\n"
+                                          "traffic_bytes_per_launch: 1e9\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
+    assert bench.read_traffic("w") == 1.5e9
+    m = bench.read_mfma("w")
+    assert m["executed_bf16_flops_per_launch"] == 2e10 and m["mfma_busy_frac"] == 0.05
+    assert bench.read_traffic("old") is None
+    assert bench.read_traffic("missing") is None and bench.read_mfma("missing") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one MI355X" in r.stderr
