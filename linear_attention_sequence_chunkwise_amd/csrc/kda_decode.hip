@@ -37,6 +37,16 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeArgs args) {
     const int h = pair % H;
     const size_t vec = static_cast<size_t>(pair) * D;  // offset of this pair in q/k/v/z/o
 
+    // state tile of this thread: rows rg + ROWG*i, columns 4cg .. 4cg+3.  Issued first, so the
+    // threads that also compute the gate do not wait for its inputs before streaming the state.
+    const int cg = tid % COLG, rg = tid / COLG;
+    f32x4_t* __restrict__ st = reinterpret_cast<f32x4_t*>(args.state + static_cast<size_t>(pair) * D * D);
+    float4 S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const f32x4_t t = __builtin_nontemporal_load(&st[(rg + ROWG * i) * COLG + cg]);
+        S[i] = make_float4(t[0], t[1], t[2], t[3]);
+    }
     // per-channel gate and inputs
     float kqp = 0.f;
     if (tid < D) {
@@ -49,15 +59,6 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeArgs args) {
         s_k[tid] = kk;
         s_q[tid] = qq;
         kqp = kk * qq;
-    }
-    // state tile of this thread: rows rg + ROWG*i, columns 4cg .. 4cg+3
-    const int cg = tid % COLG, rg = tid / COLG;
-    f32x4_t* __restrict__ st = reinterpret_cast<f32x4_t*>(args.state + static_cast<size_t>(pair) * D * D);
-    float4 S[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const f32x4_t t = __builtin_nontemporal_load(&st[(rg + ROWG * i) * COLG + cg]);
-        S[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
 
     // k.q: wave reduction, then across waves
