@@ -109,9 +109,11 @@ def cpu_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(inp, budget_s: float = 20.0):
+def cpu_baseline(inp, budget_s: float = 20.0, min_s: float = 10.0):
     """The oracle, untuned, on the host cores over a bounded sample of the same workload:
-    whole (sequence, head) pairs are added until about budget_s of estimated CPU time."""
+    whole (sequence, head) pairs are added until about budget_s of estimated CPU time.  A
+    sample that finishes much sooner (a small workload run whole) is repeated until about
+    min_s, so the rate is not a timing of a fraction of a second."""
     import oracle
     orc = oracle.load()
     threads = cpu_threads()
@@ -125,14 +127,18 @@ def cpu_baseline(inp, budget_s: float = 20.0):
     if n < len(pairs):
         n = max(1, (n // threads) * threads)
     sample = pairs[:n]   # the whole workload when it fits the budget
+    est = per_round * -(-len(sample) // threads)
+    reps = int(min(1000, max(1, min_s // max(est, 1e-3))))
     t0 = time.perf_counter()
-    _run_oracle_pairs(orc, inp, sample, threads)
+    for _ in range(reps):
+        _run_oracle_pairs(orc, inp, sample, threads)
     secs = time.perf_counter() - t0
-    tok_heads = sum(inp.lengths[n] for n, _ in sample)
+    tok_heads = reps * sum(inp.lengths[n] for n, _ in sample)
     tokens_per_s = tok_heads / secs / inp.H   # sequence tokens/s over all H heads
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sample)} of {len(pairs)} (sequence, head) pairs of the same workload, "
-                      f"{tok_heads} token-heads in {secs:.2f} s; fp64 token recurrence"}
+            "sample": f"{len(sample)} of {len(pairs)} (sequence, head) pairs of the same workload"
+                      + (f", run {reps} times" if reps > 1 else "")
+                      + f": {tok_heads} token-heads in {secs:.2f} s; fp64 token recurrence"}
 
 
 def _run_oracle_pairs(orc, inp, pairs, threads):
