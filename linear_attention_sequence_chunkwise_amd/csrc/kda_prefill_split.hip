@@ -210,6 +210,8 @@ __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
 template <int DK, typename TIn>
 __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_kernel(SplitArgs args) {
     using Smem = IntraSmem<DK>;
+    // four workgroups per CU (bf16 inputs, see the launch bounds) need their LDS to fit 160 KiB
+    static_assert(sizeof(Smem) * (sizeof(TIn) == 2 ? 4 : 2) <= 160 * 1024, "intra-chunk LDS budget");
     using P = Pair<TIn>;
     using B = Block<DK>;
     constexpr int NT = 256;
