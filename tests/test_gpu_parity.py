@@ -58,6 +58,15 @@ def test_prefill_varlen_edge_lengths():
     _check_prefill(inp)
 
 
+@pytest.mark.parametrize("dk", [64, 128])
+def test_prefill_many_heads(dk):
+    """48 heads, not a power of two: the intra-chunk grid numbers (chunk slot, head) with the
+    head fastest, so every workgroup index is split by a division by H."""
+    inp = workloads.prefill_inputs([0, 70, 129], H=48, dk=dk, dv=dk, dtype="bf16", seed=30 + dk,
+                                   s0_std=0.02, name=f"h48_d{dk}")
+    _check_prefill(inp)
+
+
 @pytest.mark.parametrize("z_mean", [-4.0, -8.0, 6.0])
 def test_prefill_stress_gates(z_mean):
     """Slow decay (state carried across many chunks) and at-bound decay (16-token sums near
