@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
                 if (g4) st_stream_f4(g4 + idx, gv);
                 if (c4) st_stream_f4(c4 + idx, acc);
             };
-            constexpr int kU = 8;
+            constexpr int kU = 4;
             int64_t t = s;
             if ((e - s) % kU == 0) {
                 // whole groups of kU tokens: each group's inputs are loaded while the previous

@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
         // the common case, a whole segment inside one sequence with its history: every load is
         // issued ahead of its use -- the history rows together, then each group of kU tokens
         // while the previous group is computed -- so each lane keeps up to 2 kU loads in flight
-        constexpr int kU = 8, kG = kSegT / kU;
+        constexpr int kU = 16, kG = kSegT / kU;
         typename V8<T>::Raw hist[HIST > 0 ? HIST : 1], raw[2][kU];
 #pragma unroll
         for (int i = 0; i < HIST; ++i) hist[i] = V8<T>::load_raw(x + (tb - HIST + i) * a.C + c0);
