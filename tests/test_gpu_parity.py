@@ -192,10 +192,11 @@ def test_gate_equal_length_batch_and_g_only():
 
 # --- decode -------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp32"), (128, "fp32")])
-def test_decode_parity(d, dtype):
-    inp = workloads.decode_inputs(N=6, H=4, dk=d, dv=d, steps=24, dtype=dtype, seed=40 + d,
-                                  z_mean=-2.0, name=f"decode_d{d}_{dtype}")
+@pytest.mark.parametrize("d,dtype,N,H", [(128, "bf16", 6, 4), (64, "fp32", 6, 4), (128, "fp32", 6, 4),
+                                         (128, "bf16", 1, 1), (64, "bf16", 5, 3)])
+def test_decode_parity(d, dtype, N, H):
+    inp = workloads.decode_inputs(N=N, H=H, dk=d, dv=d, steps=24, dtype=dtype, seed=40 + d + N,
+                                  z_mean=-2.0, name=f"decode_d{d}_{dtype}_n{N}_h{H}")
     note(f"[decode] {inp.name}")
     state = inp.S0.cuda().clone()
     A = inp.A.cuda()
