@@ -105,9 +105,26 @@ def _check(fn: str, code: int):
 
 
 def _dev(*ts):
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous and on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype: torch.dtype):
+    """The kernels take plain pointers and trust these shapes: check them before any call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
 
 
 def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
@@ -123,6 +140,12 @@ def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
         gcum = torch.empty_like(z)
     if cu_seqlens is not None:
         n_seqs = cu_seqlens.numel() - 1
+    f32 = torch.float32
+    _expect("z", z, (T, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("g", g, (T, H, dk), f32)
+    _expect("gcum", gcum, (T, H, dk), f32)
+    _expect("cu_seqlens", cu_seqlens, (n_seqs + 1,), torch.int32)
     _dev(z, A, g, gcum, cu_seqlens)
     _check("kda_gate", lib.kda_gate(_ptr(z), _ptr(A), _ptr(g), _ptr(gcum), T, H, dk,
                                     _ptr(cu_seqlens), n_seqs, chunk, g_min, _stream(stream)))
@@ -163,6 +186,23 @@ def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=Non
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    et, f32 = q.dtype, torch.float32
+    _expect("k", k, (total, H, dk), et)
+    _expect("v", v, (total, H, dv), et)
+    _expect("beta", beta, (total, H), et)
+    _expect("z", z, (total, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("initial_state", initial_state, (N, H, dk, dv), f32)
+    _expect("final_state", final_state, (N, H, dk, dv), f32)
+    _expect("cu_seqlens", cu_seqlens, (N + 1,), torch.int32)
+    _expect("o", o, (total, H, dv), et)
+    if checkpoints is not None:
+        if checkpoints.dim() != 4 or tuple(checkpoints.shape[1:]) != (H, dk, dv) or checkpoints.dtype != f32:
+            raise ValueError(f"checkpoints: expected fp32 [n_ckpt, {H}, {dk}, {dv}]")
+        if cu_seqlens is None and checkpoint_interval > 0 and \
+                checkpoints.shape[0] < N * (T_or_total // checkpoint_interval):
+            raise ValueError("checkpoints: fewer rows than the sequences' checkpoints")
+        _expect("checkpoint_offsets", checkpoint_offsets, (N + 1,), torch.int32)
     _dev(q, k, v, beta, z, A, initial_state, final_state, cu_seqlens, o, workspace, checkpoints,
          checkpoint_offsets)
     if checkpoints is not None:
@@ -187,6 +227,14 @@ def kda_decode_step(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, st
     dv = v.shape[2]
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    et, f32 = q.dtype, torch.float32
+    _expect("k", k, (N, H, dk), et)
+    _expect("v", v, (N, H, dv), et)
+    _expect("beta", beta, (N, H), et)
+    _expect("z", z, (N, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("state", state, (N, H, dk, dv), f32)
+    _expect("o", o, (N, H, dv), et)
     _dev(q, k, v, beta, z, A, state, o)
     _check("kda_decode_step", lib.kda_decode_step(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
@@ -203,6 +251,14 @@ def kda_decode_verify(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, 
     dv = v.shape[3]
     if o is None:
         o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
+    et, f32 = q.dtype, torch.float32
+    _expect("k", k, (N, K, H, dk), et)
+    _expect("v", v, (N, K, H, dv), et)
+    _expect("beta", beta, (N, K, H), et)
+    _expect("z", z, (N, K, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("state", state, (N, H, dk, dv), f32)
+    _expect("o", o, (N, K, H, dv), et)
     _dev(q, k, v, beta, z, A, state, o)
     _check("kda_decode_verify", lib.kda_decode_verify(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
@@ -216,6 +272,13 @@ def kda_decode_commit(k, v, beta, z, A, state, accepted, g_min: float = G_MIN, s
     lib = load_library()
     N, K, H, dk = k.shape
     dv = v.shape[3]
+    et, f32 = k.dtype, torch.float32
+    _expect("v", v, (N, K, H, dv), et)
+    _expect("beta", beta, (N, K, H), et)
+    _expect("z", z, (N, K, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("state", state, (N, H, dk, dv), f32)
+    _expect("accepted", accepted, (N,), torch.int32)
     _dev(k, v, beta, z, A, state, accepted)
     _check("kda_decode_commit", lib.kda_decode_commit(
         _dtype_code(k), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(state), N, K,
@@ -231,6 +294,9 @@ def kda_output_gate(o, gate, weight, eps: float = 1e-6, y=None, stream=None):
     rows = o.numel() // dv if dv else 0
     if y is None:
         y = torch.empty_like(o)
+    _expect("gate", gate, tuple(o.shape), o.dtype)
+    _expect("weight", weight, (dv,), torch.float32)
+    _expect("y", y, tuple(o.shape), o.dtype)
     _dev(o, gate, weight, y)
     _check("kda_output_gate", lib.kda_output_gate(
         _dtype_code(o), _ptr(o), _ptr(gate), _ptr(weight), float(eps), rows, dv, _ptr(y),
@@ -255,6 +321,13 @@ def kda_short_conv(x, weight, cache_in=None, cache_out=None, cu_seqlens=None,
         T_or_total = total // N
     if y is None:
         y = torch.empty_like(x)
+    f32 = torch.float32
+    _expect("weight", weight, (C, width), f32)
+    if width > 1:
+        _expect("cache_in", cache_in, (N, C, width - 1), f32)
+        _expect("cache_out", cache_out, (N, C, width - 1), f32)
+    _expect("cu_seqlens", cu_seqlens, (N + 1,), torch.int32)
+    _expect("y", y, (total, C), x.dtype)
     _dev(x, weight, cache_in, cache_out, cu_seqlens, y)
     _check("kda_short_conv", lib.kda_short_conv(
         _dtype_code(x), _ptr(x), _ptr(weight), width, _ptr(cache_in), _ptr(cache_out),

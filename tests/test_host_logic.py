@@ -147,3 +147,80 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one MI355X" in r.stderr
+
+
+# --- binding argument checks -------------------------------------------------------------
+# The kernels take plain pointers, so the binding checks every tensor's shape and dtype
+# against the call's sizes before anything is launched (these raise on the CPU, before the
+# device check).
+
+def _prefill_args(T=64, H=2, d=64):
+    bf = torch.bfloat16
+    return dict(q=torch.zeros(T, H, d, dtype=bf), k=torch.zeros(T, H, d, dtype=bf),
+                v=torch.zeros(T, H, d, dtype=bf), beta=torch.zeros(T, H, dtype=bf),
+                z=torch.zeros(T, H, d), A=torch.zeros(H, d))
+
+
+def test_binding_rejects_mismatched_prefill_tensors():
+    from linear_attention_sequence_chunkwise_amd import kda
+    bad = [("v", torch.zeros(63, 2, 64, dtype=torch.bfloat16), "v: shape"),
+           ("beta", torch.zeros(64, 2, 1, dtype=torch.bfloat16), "beta: shape"),
+           ("z", torch.zeros(64, 2, 64, dtype=torch.bfloat16), "z: dtype"),
+           ("A", torch.zeros(2, 32), "A: shape"),
+           ("k", torch.zeros(64, 2, 64), "k: dtype")]
+    for name, t, msg in bad:
+        a = _prefill_args()
+        a[name] = t
+        with pytest.raises(ValueError, match=msg):
+            kda.kda_prefill_fwd(**a)
+    with pytest.raises(ValueError, match="initial_state: shape"):
+        kda.kda_prefill_fwd(**_prefill_args(), initial_state=torch.zeros(2, 2, 64, 64))
+    with pytest.raises(ValueError, match="o: shape"):
+        kda.kda_prefill_fwd(**_prefill_args(), o=torch.zeros(64, 2, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="cu_seqlens: dtype"):
+        kda.kda_prefill_fwd(**_prefill_args(), cu_seqlens=torch.tensor([0, 64]))
+    with pytest.raises(ValueError, match="checkpoints"):
+        kda.kda_prefill_fwd(**_prefill_args(), checkpoints=torch.zeros(0, 2, 64, 64),
+                            checkpoint_interval=64)
+    with pytest.raises(ValueError, match="GPU"):   # right shapes: only the device is wrong
+        kda.kda_prefill_fwd(**_prefill_args())
+
+
+def test_binding_rejects_mismatched_decode_tensors():
+    from linear_attention_sequence_chunkwise_amd import kda
+    bf = torch.bfloat16
+    N, K, H, d = 3, 2, 2, 64
+    q = torch.zeros(N, H, d, dtype=bf)
+    args = dict(k=q.clone(), v=q.clone(), beta=torch.zeros(N, H, dtype=bf),
+                z=torch.zeros(N, H, d), A=torch.zeros(H, d))
+    with pytest.raises(ValueError, match="state: shape"):
+        kda.kda_decode_step(q, **args, state=torch.zeros(N, H, d, 32))
+    with pytest.raises(ValueError, match="z: dtype"):
+        kda.kda_decode_step(q, **{**args, "z": torch.zeros(N, H, d, dtype=bf)},
+                            state=torch.zeros(N, H, d, d))
+    qk = torch.zeros(N, K, H, d, dtype=bf)
+    margs = dict(v=qk.clone(), beta=torch.zeros(N, K, H, dtype=bf), z=torch.zeros(N, K, H, d),
+                 A=torch.zeros(H, d), state=torch.zeros(N, H, d, d))
+    with pytest.raises(ValueError, match="k: shape"):
+        kda.kda_decode_verify(qk, torch.zeros(N, K + 1, H, d, dtype=bf), **margs)
+    with pytest.raises(ValueError, match="accepted: dtype"):
+        kda.kda_decode_commit(qk, **margs, accepted=torch.zeros(N, dtype=torch.int64))
+
+
+def test_binding_rejects_mismatched_elementwise_tensors():
+    from linear_attention_sequence_chunkwise_amd import kda
+    with pytest.raises(ValueError, match="A: shape"):
+        kda.kda_gate(torch.zeros(8, 2, 64), torch.zeros(3, 64))
+    with pytest.raises(ValueError, match="g: dtype"):
+        kda.kda_gate(torch.zeros(8, 2, 64), torch.zeros(2, 64),
+                     g=torch.zeros(8, 2, 64, dtype=torch.bfloat16))
+    o = torch.zeros(10, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="gate: dtype"):
+        kda.kda_output_gate(o, torch.zeros(10, 128), torch.ones(128))
+    with pytest.raises(ValueError, match="weight: shape"):
+        kda.kda_output_gate(o, o.clone(), torch.ones(64))
+    x = torch.zeros(70, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="weight: shape"):
+        kda.kda_short_conv(x, torch.zeros(128, 4))
+    with pytest.raises(ValueError, match="cache_in: shape"):
+        kda.kda_short_conv(x, torch.zeros(256, 4), cache_in=torch.zeros(1, 256, 4))
