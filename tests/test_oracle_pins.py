@@ -70,6 +70,19 @@ def test_sixteen_token_tile_bound(oracle_lib, z_mean):
     assert math.exp(G16.min()) > FP32_MIN_NORMAL
 
 
+@pytest.mark.parametrize("name", ["prefill_b1_h2_t256_d64_fp32", "prefill_b1_h16_t4096_d128_bf16"])
+def test_sixteen_token_tile_bound_on_named_workloads(oracle_lib, name):
+    """The bound on the seeded inputs of the named workloads themselves (the larger ones
+    are several GB; the bound holds for any data once g >= -5, which the gate pins fix)."""
+    from linear_attention_sequence_chunkwise_amd import workloads
+    inp = workloads.make(name)
+    g = oracle_lib.gate(inp.z.numpy(), inp.A.numpy())
+    assert g.min() >= -5.0 and g.max() <= 0.0
+    G16 = oracle_lib.chunk_cumsum(g, inp.cu_seqlens.numpy(), chunk=16)
+    assert G16.min() >= -80.0 and G16.max() <= 0.0
+    assert math.exp(-G16.min()) < BF16_MAX and math.exp(G16.min()) > FP32_MIN_NORMAL
+
+
 def test_bound_negative_controls(oracle_lib):
     """A single 64-token reference would overflow, and an unbounded gate breaks the
     16-token bound: the tile structure and the lower bound are both needed."""
