@@ -83,6 +83,8 @@ typedef enum kda_dtype {
  *   chunk       1 .. KDA_GATE_MAX_CHUNK (the prefill uses 64)
  *   g_min       finite and < 0 (the pages fix -5)
  *   dk          a multiple of 4; total_tokens >= 0; H >= 1; n_seqs >= 1
+ * KDA_ERR_SHAPE also when ceil(total_tokens / chunk) * ceil(H * dk / 1024) exceeds 2^24 - 1
+ * (one 256-thread workgroup per window of chunk tokens and 1024 channels).
  */
 kda_status kda_gate(const float* z, const float* A, float* g, float* gcum,
                     int64_t total_tokens, int H, int dk, const int32_t* cu_seqlens,
@@ -256,6 +258,8 @@ kda_status kda_output_gate(kda_dtype dt, const void* o, const void* gate, const 
  *   cu_seqlens  device int32 [N + 1], or NULL for N sequences of T_or_total tokens
  *   l2_group    0, 64 or 128 (C a multiple of it)
  *   y           [total, C] of type dt; must not be x
+ * KDA_ERR_SHAPE also when ceil(total / 64) * ceil(C / 2048) exceeds 2^24 - 1 (one 256-thread
+ * workgroup per 64-token segment and 2048 channels).
  */
 kda_status kda_short_conv(kda_dtype dt, const void* x, const float* weight, int width,
                           const float* cache_in, float* cache_out, const int32_t* cu_seqlens,
