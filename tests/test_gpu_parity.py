@@ -156,7 +156,8 @@ def _gate_tol(chunk):
 # one partial
 @pytest.mark.parametrize("lens,chunk,H", [([300], 64, 3), ([0, 5, 64, 0, 130, 1, 77], 64, 3),
                                           ([1000, 333], 16, 3), ([129, 64, 65], 100, 3),
-                                          ([0, 5, 64, 0, 130, 1, 77], 64, 11)])
+                                          ([0, 5, 64, 0, 130, 1, 77], 64, 11),
+                                          ([130, 7], 1, 3), ([5000, 3], 1024, 2)])
 def test_gate_parity(lens, chunk, H):
     rng = np.random.default_rng(sum(lens) + chunk + H)
     T, dk = int(sum(lens)), 128
@@ -173,6 +174,8 @@ def test_gate_parity(lens, chunk, H):
     e_g, e_c = max_abs(g.cpu().numpy(), g_ref), max_abs(gc.cpu().numpy(), gc_ref)
     note(f"    max|dg| = {e_g:.2e}  max|dGamma| = {e_c:.2e}  (tol {_gate_tol(chunk):.2e})")
     assert e_g <= 1e-5 and e_c <= _gate_tol(chunk)
+    if chunk == 1:  # one-token chunks: the cumulative sum is the gate itself
+        assert torch.equal(g, gc)
 
 
 def test_gate_equal_length_batch_and_g_only():
