@@ -58,6 +58,25 @@ def test_prefill_varlen_edge_lengths():
     _check_prefill(inp)
 
 
+def _many_short_lengths(n, seed):
+    """n sequence lengths in [0, 70] with every edge present: empty, one token, one chunk less
+    one token, exactly one chunk, one chunk plus one token."""
+    lens = np.random.default_rng(seed).integers(0, 71, n)
+    lens[:5] = [0, 1, 63, 64, 65]
+    return [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("dk,dtype", [(128, "bf16"), (64, "fp32")])
+def test_prefill_many_short_sequences(dk, dtype):
+    """1,500 short ragged sequences: the chunk table's scan runs over two 1,024-sequence blocks
+    with a carry, the intra-chunk grid searches 1,500 sequence starts, and the state pass runs
+    3,000 chains (pairs not a multiple of the 8 XCDs)."""
+    inp = workloads.prefill_inputs(_many_short_lengths(1500, 40 + dk), H=2, dk=dk, dv=dk,
+                                   dtype=dtype, seed=41 + dk, s0_std=0.02,
+                                   name=f"n1500_short_d{dk}_{dtype}")
+    _check_prefill(inp)
+
+
 @pytest.mark.parametrize("dk", [64, 128])
 def test_prefill_many_heads(dk):
     """48 heads, not a power of two: the intra-chunk grid numbers (chunk slot, head) with the
@@ -176,6 +195,26 @@ def test_gate_parity(lens, chunk, H):
     assert e_g <= 1e-5 and e_c <= _gate_tol(chunk)
     if chunk == 1:  # one-token chunks: the cumulative sum is the gate itself
         assert torch.equal(g, gc)
+
+
+def test_gate_many_short_sequences():
+    """1,100 short sequences, some empty: each window's first sequence is found by a binary
+    search over the sequence starts, and windows hold many chunk starts."""
+    lens = _many_short_lengths(1100, 9)
+    rng = np.random.default_rng(10)
+    T, H, dk = int(sum(lens)), 2, 128
+    z = rng.normal(0, 2, (T, H, dk)).astype(np.float32)
+    A = rng.normal(0, 0.5, (H, dk)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    note(f"[gate] {len(lens)} sequences, {T} tokens, chunk 64")
+    g, gc = kda.kda_gate(torch.from_numpy(z).cuda(), torch.from_numpy(A).cuda(),
+                         cu_seqlens=torch.from_numpy(cu).cuda(), chunk=64)
+    torch.cuda.synchronize()
+    orc = oracle.load()
+    g_ref = orc.gate(z, A)
+    gc_ref = orc.chunk_cumsum(g_ref, cu, chunk=64)
+    assert max_abs(g.cpu().numpy(), g_ref) <= 1e-5
+    assert max_abs(gc.cpu().numpy(), gc_ref) <= _gate_tol(64)
 
 
 def test_gate_equal_length_batch_and_g_only():
