@@ -60,6 +60,21 @@ def test_short_conv_varlen_parity(C, width, l2, dtype):
     note(f"[short conv] C={C} width={width} l2={l2} {dtype}: max|dy| = {e:.3e}")
 
 
+def test_short_conv_many_short_sequences():
+    """1,100 sequences of 0-5 tokens at width 4: most windows reach into the cache, and the
+    cache out of a sequence shorter than width - 1 keeps part of the cache in."""
+    lengths = [int(x) for x in np.random.default_rng(12).integers(0, 6, 1100)]
+    lengths[:6] = [0, 1, 2, 3, 4, 5]
+    C, width, l2, dtype = 256, 4, 128, torch.bfloat16
+    x, w, cache, cu = _inputs(lengths, C, width, dtype, seed=77)
+    co = torch.full((len(lengths), C, width - 1), float("nan")).cuda()
+    y = kda.kda_short_conv(x.cuda(), w.cuda(), cache_in=cache.cuda(), cache_out=co,
+                           cu_seqlens=cu.cuda(), l2_group=l2)
+    torch.cuda.synchronize()
+    e = _check(y, co, x, w, cache, cu, l2, dtype)
+    note(f"[short conv] 1,100 short sequences, {int(sum(lengths))} tokens: max|dy| = {e:.3e}")
+
+
 def test_short_conv_equal_length_without_cache():
     x, w, _, cu = _inputs([70, 70, 70], 512, 4, torch.bfloat16, seed=7, with_cache=False)
     y = kda.kda_short_conv(x.cuda(), w.cuda(), n_seqs=3, l2_group=128)
