@@ -60,7 +60,8 @@ def _run(inp, interval, use_cu):
 
 
 def _check(inp, interval, use_cu):
-    note(f"[checkpoints] {inp.name} lens={inp.lengths} interval={interval} use_cu={use_cu}")
+    note(f"[checkpoints] {inp.name} lens={inp.lengths[:8]}{'...' if inp.N > 8 else ''} "
+         f"interval={interval} use_cu={use_cu}")
     o, sN, ck, counts, offs = _run(inp, interval, use_cu)
     refs = _truncated_reference(inp, interval)
     assert len(refs) == int(offs[-1])
@@ -94,6 +95,16 @@ def test_checkpoints_varlen_edge_lengths():
     inp = workloads.prefill_inputs([100, 128, 0, 300, 512, 65], H=2, dk=128, dv=128,
                                    dtype="bf16", seed=32, s0_std=0.02, name="ck_varlen")
     _check(inp, 128, use_cu=True)
+
+
+def test_checkpoints_many_sequences():
+    """300 sequences of 0-200 tokens (600 chains): the state pass runs its four-compute-wave
+    form, and most sequences hold zero to three checkpoints at their own offsets."""
+    lens = [int(x) for x in np.random.default_rng(35).integers(0, 201, 300)]
+    lens[:4] = [0, 64, 63, 128]
+    inp = workloads.prefill_inputs(lens, H=2, dk=128, dv=128, dtype="bf16", seed=35,
+                                   s0_std=0.02, name="ck_many")
+    _check(inp, 64, use_cu=True)
 
 
 def test_checkpoints_d64_fp32():
