@@ -96,3 +96,46 @@ def test_decode_n512_h32_256_steps_sampled():
     es = state_rel_err(Sg, S_ref)
     note(f"    256 steps: max|do| = {worst:.3e}  rel dS = {es:.3e}")
     assert worst <= OUT_TOL and es <= STATE_TOL
+
+
+def test_spec_decode_n512_h32_k4_sampled():
+    """One speculative round at the timed size (512 sequences x 32 heads, d = 128, bf16, K = 4):
+    verify's per-position outputs and commit's states for accepted counts 0..4 (and one
+    value above K, which clamps to K), on sampled (sequence, head) pairs."""
+    K = 4
+    d = workloads.decode_inputs(N=512, H=32, dk=128, dv=128, steps=K, dtype="bf16", seed=5,
+                                name="spec_decode_n512_h32_d128_bf16")
+    note(f"[full] {d.name} K={K}")
+    nk = lambda x: x.transpose(0, 1).contiguous().cuda()  # [K, N, ...] -> [N, K, ...]
+    q, k, v, beta, z = (nk(t) for t in (d.q, d.k, d.v, d.beta, d.z))
+    A = d.A.cuda()
+    state = d.S0.cuda()
+    rng = np.random.default_rng(6)
+    acc = rng.integers(0, K + 1, d.N).astype(np.int32)
+    pairs = [(0, 0), (511, 31), (100, 7), (257, 20), (33, 31), (400, 2)]
+    for (n, _), a in zip(pairs, [0, 4, 7, 1, 2, 3]):
+        acc[n] = a
+    o = kda.kda_decode_verify(q, k, v, beta, z, A, state)
+    torch.cuda.synchronize()
+    og = np.stack([o[n, :, h].float().cpu().numpy() for n, h in pairs])  # [P, K, dv]
+    untouched = all(torch.equal(state[n, h], d.S0[n, h].cuda()) for n, h in pairs)
+    kda.kda_decode_commit(k, v, beta, z, A, state, torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+
+    pa = np.array(pairs, dtype=np.int32)
+    S_ref = np.ascontiguousarray(np.stack([d.S0[n, h].numpy() for n, h in pairs]).astype(np.float64))
+    orc = oracle.load()
+    f = lambda t: t.float().numpy()
+    o_ref, snaps = [], [S_ref.copy()]
+    for t in range(K):
+        o_ref.append(orc.decode_step(f(d.q[t]), f(d.k[t]), f(d.v[t]), f(d.beta[t]), d.z[t].numpy(),
+                                     d.A.numpy(), S_ref, pairs=pa))
+        snaps.append(S_ref.copy())
+    e_o = max_abs(og, np.stack(o_ref, 1))
+    S_want = np.stack([snaps[min(int(acc[n]), K)][i] for i, (n, _) in enumerate(pairs)])
+    Sg = np.stack([state[n, h].cpu().numpy() for n, h in pairs])
+    e_s = state_rel_err(Sg, S_want)
+    note(f"    verify max|do| = {e_o:.3e}   commit rel dS = {e_s:.3e}")
+    assert untouched
+    assert e_o <= OUT_TOL and e_o <= 2e-3
+    assert e_s <= STATE_TOL and e_s <= 1e-4
