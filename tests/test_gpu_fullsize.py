@@ -139,3 +139,92 @@ def test_spec_decode_n512_h32_k4_sampled():
     assert untouched
     assert e_o <= OUT_TOL and e_o <= 2e-3
     assert e_s <= STATE_TOL and e_s <= 1e-4
+
+
+# --- standalone kernels at the sizes bench.py times (inputs drawn on the host, seeded) ------
+
+def _gate_tol(chunk):
+    return chunk * float(np.spacing(np.float32(5.0 * chunk))) / 2 + chunk * 1e-5
+
+
+def test_gate_b4_t32768_h32_sampled():
+    """kda_gate with the chunk-local cumulative sum over 4 x 32768 tokens x 32 heads x 128
+    channels (fp32), checked on whole sampled chunks: first and last of a sequence, across a
+    sequence boundary, and inside."""
+    N, T, H, dk = 4, 32768, 32, 128
+    gen = torch.Generator().manual_seed(11)
+    z = torch.randn(N * T, H, dk, generator=gen)
+    A = torch.randn(H, dk, generator=gen) * 0.5
+    note(f"[full] gate b4 t32768 h32 d128 f32")
+    g, gc = kda.kda_gate(z.cuda(), A.cuda(), n_seqs=N)
+    torch.cuda.synchronize()
+    orc = oracle.load()
+    worst_g = worst_c = 0.0
+    for s in (0, T - 64, T, 2 * T + 640, N * T - 64):
+        zs = z[s:s + 64].numpy()
+        g_ref = orc.gate(zs, A.numpy())
+        c_ref = orc.chunk_cumsum(g_ref, np.array([0, 64], dtype=np.int32), chunk=64)
+        worst_g = max(worst_g, max_abs(g[s:s + 64].cpu().numpy(), g_ref))
+        worst_c = max(worst_c, max_abs(gc[s:s + 64].cpu().numpy(), c_ref))
+    note(f"    max|dg| = {worst_g:.2e}  max|dGamma| = {worst_c:.2e}")
+    assert worst_g <= 1e-5 and worst_c <= _gate_tol(64)
+
+
+def test_output_gate_rows4194304_sampled():
+    """kda_output_gate over 4 x 32768 x 32 rows of d_v = 128 (bf16), sampled rows."""
+    rows, dv = 4 * 32768 * 32, 128
+    gen = torch.Generator().manual_seed(6)
+    o = (torch.randn(rows, dv, generator=gen) * 0.05).to(torch.bfloat16)
+    gate = torch.randn(rows, dv, generator=gen).to(torch.bfloat16)
+    w = 1.0 + 0.1 * torch.randn(dv, generator=gen)
+    note(f"[full] output gate rows={rows} dv={dv} bf16")
+    y = kda.kda_output_gate(o.cuda(), gate.cuda(), w.cuda(), eps=1e-6)
+    torch.cuda.synchronize()
+    idx = np.concatenate([np.arange(1024), np.arange(rows - 1024, rows),
+                          np.random.default_rng(8).integers(0, rows, 4096)])
+    it = torch.from_numpy(idx)
+    ref = oracle.load().output_gate(o[it].float().numpy(), gate[it].float().numpy(), w.numpy(), eps=1e-6)
+    got = y[it.cuda()].float().cpu().numpy()
+    d = np.abs(got - ref)
+    note(f"    {len(idx)} rows: max|dy| = {d.max():.3e}")
+    assert d.max() <= OUT_TOL
+    assert np.all(d <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+def test_short_conv_b4_t32768_c4096_sampled():
+    """kda_short_conv (width 4, per-head L2Norm over 128 channels, caches in and out) over
+    4 x 32768 tokens x 4096 channels (bf16).  Checked: each sequence's first 16 tokens (their
+    windows reach into the cache), 16-token runs inside, and every cache out exactly."""
+    N, T, C, width = 4, 32768, 32 * 128, 4
+    gen = torch.Generator().manual_seed(7)
+    x = torch.randn(N * T, C, generator=gen).to(torch.bfloat16)
+    w = torch.randn(C, width, generator=gen) * 0.5
+    cache = torch.randn(N, C, width - 1, generator=gen).to(torch.bfloat16).float()
+    note(f"[full] short conv b4 t32768 c4096 w4 bf16")
+    co = torch.full((N, C, width - 1), float("nan"), device="cuda")
+    y = kda.kda_short_conv(x.cuda(), w.cuda(), cache_in=cache.cuda(), cache_out=co, n_seqs=N,
+                           l2_group=128)
+    torch.cuda.synchronize()
+    orc = oracle.load()
+    worst = 0.0
+    for n in range(N):
+        s = n * T
+        # the first 16 tokens, with this sequence's cache
+        ref, _ = orc.short_conv(x[s:s + 16].float().numpy(), w.numpy(), cache[n:n + 1].numpy(),
+                                cu_seqlens=np.array([0, 16], np.int32), l2_group=128)
+        runs = [(s, ref)]
+        # 16 tokens inside: the window of token t needs t-3 .. t, so the run starts 3 early
+        t = s + 1000 + 7919 * n
+        ref, _ = orc.short_conv(x[t - 3:t + 16].float().numpy(), w.numpy(), None,
+                                cu_seqlens=np.array([0, 19], np.int32), l2_group=128)
+        runs.append((t, ref[3:]))
+        for t0, r in runs:
+            got = y[t0:t0 + 16].float().cpu().numpy()
+            d = np.abs(got - r)
+            worst = max(worst, float(d.max()))
+            assert np.all(d <= 2.0 ** -8 * np.abs(r) + 1e-5)
+        # cache out: the sequence's last width - 1 inputs, channel-major
+        want = x[s + T - (width - 1):s + T].float().numpy().T
+        assert np.array_equal(co[n].cpu().numpy(), want)
+    note(f"    max|dy| = {worst:.3e}")
+    assert worst <= OUT_TOL
