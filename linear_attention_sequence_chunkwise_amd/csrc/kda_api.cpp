@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -25,18 +26,20 @@ bool supported_d(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // far beyond any device memory
 
+// CU count of the calling thread's current device, queried once per device.  Atomic entries:
+// calls from several host threads may fill the same entry at once (with the same value).
 int compute_units() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
 
 }  // namespace
