@@ -279,3 +279,47 @@ def test_decode_matches_prefill_of_the_same_tokens():
     torch.cuda.synchronize()
     assert max_abs(od.float().cpu().numpy(), op.float().cpu().numpy()) <= OUT_TOL
     assert state_rel_err(state.cpu().numpy(), sN.cpu().numpy()) <= STATE_TOL
+
+
+# --- gate floors other than -5 (any g_min in [-5, 0) keeps the 16-token bound) ------------
+
+@pytest.mark.parametrize("g_min", [-0.5, -2.5])
+def test_prefill_and_decode_other_gate_floor(g_min):
+    """g_min enters the gate of every kernel: the prefill (varlen, initial state, bf16 d128),
+    the standalone gate, and a decode step, each compared with the oracle at the same floor
+    on seeded inputs."""
+    inp = workloads.prefill_inputs([130, 0, 64, 7], H=3, dk=128, dv=128, dtype="bf16", seed=81,
+                                   s0_std=0.02, name=f"gmin{g_min}")
+    note(f"[g_min {g_min}] prefill {inp.lengths}, gate, decode")
+    c = lambda t: t.cuda()
+    sN = torch.empty((inp.N, inp.H, inp.dk, inp.dv), device="cuda")
+    o = kda.kda_prefill_fwd(c(inp.q), c(inp.k), c(inp.v), c(inp.beta), c(inp.z), c(inp.A),
+                            g_min=g_min, initial_state=c(inp.S0), final_state=sN,
+                            cu_seqlens=c(inp.cu_seqlens))
+    g, gc = kda.kda_gate(c(inp.z), c(inp.A), cu_seqlens=c(inp.cu_seqlens), chunk=64, g_min=g_min)
+    torch.cuda.synchronize()
+    orc = oracle.load()
+    f = lambda t: t.float().numpy()
+    o_ref, S_ref = orc.prefill(f(inp.q), f(inp.k), f(inp.v), f(inp.beta), z=inp.z.numpy(),
+                               A=inp.A.numpy(), g_min=g_min, S0=inp.S0.numpy(),
+                               cu_seqlens=inp.cu_seqlens.numpy())
+    e_o = max_abs(o.float().cpu().numpy().astype(np.float64), o_ref)
+    e_s = state_rel_err(sN.cpu().numpy(), S_ref)
+    g_ref = orc.gate(inp.z.numpy(), inp.A.numpy(), g_min=g_min)
+    assert max_abs(g.cpu().numpy(), g_ref) <= 1e-5
+    assert max_abs(gc.cpu().numpy(), orc.chunk_cumsum(g_ref, inp.cu_seqlens.numpy(), 64)) <= _gate_tol(64)
+    # one decode step at the same floor, from the decode workload's own seeded state
+    dec = workloads.decode_inputs(N=inp.N, H=inp.H, dk=128, dv=128, steps=1, dtype="bf16",
+                                  seed=82, name="gmin_decode")
+    state = dec.S0.cuda()
+    od = kda.kda_decode_step(c(dec.q[0]), c(dec.k[0]), c(dec.v[0]), c(dec.beta[0]), c(dec.z[0]),
+                             c(dec.A), state, g_min=g_min)
+    torch.cuda.synchronize()
+    S_dec = dec.S0.numpy().astype(np.float64)
+    od_ref = orc.decode_step(f(dec.q[0]), f(dec.k[0]), f(dec.v[0]), f(dec.beta[0]),
+                             dec.z[0].numpy(), dec.A.numpy(), S_dec, g_min=g_min)
+    e_d = max_abs(od.float().cpu().numpy(), od_ref)
+    e_ds = state_rel_err(state.cpu().numpy(), S_dec)
+    note(f"    prefill max|do| = {e_o:.3e} rel dS = {e_s:.3e}; decode max|do| = {e_d:.3e} rel dS = {e_ds:.3e}")
+    assert e_o <= OUT_TOL and e_s <= STATE_TOL and e_o <= GUARD_OUT and e_s <= GUARD_STATE
+    assert e_d <= 2e-3 and e_ds <= 1e-4
