@@ -34,6 +34,8 @@
 //   the lane-order image (lane_off, kn_off) that the state pass copies verbatim into LDS,
 //   T and M as their 10 lower 16x16 blocks (row-major, block order (a,b) = a(a+1)/2 + b),
 //   decayN [DK] fp32 = e^{Gamma_n}; order Qt, M | Kt, KnT, T, decayN (struct Block).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -719,6 +721,12 @@ __device__ __forceinline__ StageLoader<DK, DVS, TIn, NLW> make_loader(const Spli
     return ld;
 }
 
+// x of lane L of this lane's row of 16 lanes (DPP row broadcast)
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xf, 0xf, false));
+}
+
 template <int DK, int NCW, int NLW, typename TIn>
 __global__ void __launch_bounds__(64 * (NCW + NLW)) prefill_state_kernel(SplitArgs args) {
     constexpr int DVS = 16 * NCW;  // columns per workgroup (16 per compute wave)
@@ -827,9 +835,9 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) prefill_state_kernel(SplitAr
                 if constexpr (sizeof(TIn) == 2) vv[a][r] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(vp));
                 else vv[a][r] = *reinterpret_cast<const float*>(vp);
             }
-        float4 bb[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) bb[a] = *reinterpret_cast<const float4*>(&b.beta[16 * a + 4 * g]);
+        // beta[16a + 4g + r], read once per row of 16 lanes (lane li holds a = li / 4, r = li % 4)
+        // and spread over the row by DPP broadcasts below, instead of a 16-fold broadcast read
+        const float bsrc = b.beta[16 * (li >> 2) + 4 * g + (li & 3)];
         __builtin_amdgcn_sched_barrier(0);
         // X = K~ S: X[a][r] = X[16a + 4g + r][col li]
         f32x4_t X[4] = {zero, zero, zero, zero};
@@ -855,6 +863,11 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) prefill_state_kernel(SplitAr
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int a = 0; a < 4; ++a) Yt[a] = mfma32(Sb[s], opd[a][s], Yt[a]);
+        float4 bb[4];
+        bb[0] = make_float4(row_bcast<0>(bsrc), row_bcast<1>(bsrc), row_bcast<2>(bsrc), row_bcast<3>(bsrc));
+        bb[1] = make_float4(row_bcast<4>(bsrc), row_bcast<5>(bsrc), row_bcast<6>(bsrc), row_bcast<7>(bsrc));
+        bb[2] = make_float4(row_bcast<8>(bsrc), row_bcast<9>(bsrc), row_bcast<10>(bsrc), row_bcast<11>(bsrc));
+        bb[3] = make_float4(row_bcast<12>(bsrc), row_bcast<13>(bsrc), row_bcast<14>(bsrc), row_bcast<15>(bsrc));
         // R = beta (V - X).  Rows past the chunk's end are zero without a test: the v copy
         // writes zeros there, beta reads as zero, and K~ rows are zero, so X is zero too.
         uint2 Rb[4];
@@ -886,14 +899,37 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) prefill_state_kernel(SplitAr
         __builtin_amdgcn_sched_barrier(0);
         // S = diag(e^{Gamma_n}) S + K^n^T U
         uint4 kk[2][MT];
-        float4 dn[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             kk[0][m] = kn[(m * 2 + 0) * 64 + lane];
             kk[1][m] = kn[(m * 2 + 1) * 64 + lane];
-            dn[m] = *reinterpret_cast<const float4*>(&dnv[32 * (m >> 1) + 8 * g + 4 * (m & 1)]);
         }
+        // e^{Gamma_n} of state row 32 (j / 8) + 8 g + j % 8 for j = 4 m + r: lane li of a row
+        // reads j = 2 li, 2 li + 1 (wrapped inside the DK rows; at DK = 64 lanes 8..15 are
+        // unused), then DPP broadcasts spread them over the row
+        const float2 dsrc = *reinterpret_cast<const float2*>(
+            &dnv[32 * ((li >> 2) & (DK / 32 - 1)) + 8 * g + 2 * (li & 3)]);
         __builtin_amdgcn_sched_barrier(0);
+        float4 dn[MT];
+        auto dj = [&](auto J) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            return row_bcast<j / 2>((j & 1) ? dsrc.y : dsrc.x);
+        };
+        auto dn4 = [&](auto M) __attribute__((always_inline)) {
+            constexpr int m = decltype(M)::value;
+            return make_float4(dj(std::integral_constant<int, 4 * m>{}), dj(std::integral_constant<int, 4 * m + 1>{}),
+                               dj(std::integral_constant<int, 4 * m + 2>{}), dj(std::integral_constant<int, 4 * m + 3>{}));
+        };
+        dn[0] = dn4(std::integral_constant<int, 0>{});
+        dn[1] = dn4(std::integral_constant<int, 1>{});
+        dn[2] = dn4(std::integral_constant<int, 2>{});
+        dn[3] = dn4(std::integral_constant<int, 3>{});
+        if constexpr (MT > 4) {
+            dn[4] = dn4(std::integral_constant<int, 4>{});
+            dn[5] = dn4(std::integral_constant<int, 5>{});
+            dn[6] = dn4(std::integral_constant<int, 6>{});
+            dn[7] = dn4(std::integral_constant<int, 7>{});
+        }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             S[m][0] *= dn[m].x;
