@@ -721,7 +721,8 @@ __device__ __forceinline__ StageLoader<DK, DVS, TIn, NLW> make_loader(const Spli
     return ld;
 }
 
-// x of lane L of this lane's row of 16 lanes (DPP row broadcast)
+// x of lane L of this lane's row of 16 lanes: DPP control row_newbcast:L (0x150 + L), a
+// CDNA3/CDNA4 broadcast within each row
 template <int L>
 __device__ __forceinline__ float row_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xf, 0xf, false));
