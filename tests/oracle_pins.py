@@ -317,6 +317,37 @@ def pin_decode_equals_prefill(orc):
     _close(S, Sp, 0.0, "decode vs prefill S")
 
 
+def pin_unit_retention_is_plain_delta_rule(orc):
+    """alpha = 1 (g = 0) turns the recurrence of [K3 note] §3.1 into the plain delta rule of
+    the same section: predict vhat = S^T k, correct S <- S + beta k (v - vhat)^T, read
+    o = S^T q after the correction.  The gate reaches g = 0 exactly: e^A z = -1e4 e^A makes
+    Sigmoid underflow to 0.  Checked with and without an initial state, and through both the
+    (z, A) and the explicit-g entry of the oracle."""
+    rng = np.random.default_rng(24)
+    for L, dk, dv, with_s0 in [(24, 6, 5, True), (31, 8, 8, False), (9, 3, 7, True)]:
+        q = rng.standard_normal((L, 1, dk)).astype(np.float32)
+        k = rng.standard_normal((L, 1, dk)).astype(np.float32)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((L, 1, dv)).astype(np.float32)
+        beta = rng.uniform(0.05, 0.95, (L, 1)).astype(np.float32)
+        S0 = rng.standard_normal((1, 1, dk, dv)).astype(np.float32) if with_s0 else None
+        z = np.full((L, 1, dk), -1e4, np.float32)
+        A = rng.normal(0, 0.5, (1, dk)).astype(np.float32)
+        assert np.all(orc.gate(z, A) == 0.0), "gate at z = -1e4 is not exactly 0"
+        # the delta rule, written out on its own
+        S = np.zeros((dk, dv)) if S0 is None else S0[0, 0].astype(np.float64)
+        o_want = np.empty((L, dv))
+        for t in range(L):
+            kt = k[t, 0].astype(np.float64)
+            vhat = S.T @ kt
+            S = S + float(beta[t, 0]) * np.outer(kt, v[t, 0].astype(np.float64) - vhat)
+            o_want[t] = S.T @ q[t, 0].astype(np.float64)
+        for o, Sg in (orc.prefill(q, k, v, beta, z=z, A=A, S0=S0),
+                      orc.prefill(q, k, v, beta, g=np.zeros((L, 1, dk)), S0=S0)):
+            _close(o[:, 0], o_want, 1e-13, f"delta rule o (L={L})")
+            _close(Sg[0, 0], S, 1e-13, f"delta rule S (L={L})")
+
+
 def pin_linearity(orc):
     """o and S are jointly linear in (S0, v): scaling both by 2 scales o and S by 2."""
     rng = np.random.default_rng(23)
@@ -333,6 +364,7 @@ ALL_PINS = [
     pin_gate_in_recurrence, pin_zero_beta_zero_state, pin_unit_edit_reads_back_value,
     pin_no_write_pure_decay, pin_one_hot_keys, pin_chunked_equals_recurrent, pin_split_resume,
     pin_varlen_equals_per_sequence, pin_decode_equals_prefill, pin_linearity,
+    pin_unit_retention_is_plain_delta_rule,
 ]
 
 
