@@ -4,7 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one kda_prefill_fwd call over the named prefill workload (gate, intra-chunk
-products, triangular solve, state pass and outputs all run inside it).  The same line also
+products, triangular solve, state pass and outputs all run inside it).  The headline
+workload is the largest one, the varlen batch of 64 sequences (about 278K tokens, 32 heads,
+initial and final states); the batched (4 x 32768) and single-sequence (4096) workloads are
+timed after it and reported under 'prefill_other', each with its own roofline.  The same line also
 carries the decode half of the metric: 256 consecutive kda_decode_step calls over
 512 sequences x 32 heads, a speculative-decode round, and standalone timings of the output
 epilogue, the input prologue and the gate at the batched workload's sizes.  Inputs are seeded
@@ -110,63 +113,157 @@ def cpu_threads() -> int:
 
 
 def cpu_baseline(inp, budget_s: float = 20.0, min_s: float = 10.0):
-    """The oracle, untuned, on the host cores over a bounded sample of the same workload:
-    whole (sequence, head) pairs are added until about budget_s of estimated CPU time.  A
+    """The oracle, untuned, on the host cores over a bounded sample of the same workload: the
+    first whole sequences (all heads) up to about budget_s of estimated CPU time, converted to
+    the oracle's fp32 inputs before the clock starts; one oracle call over them is timed.  A
     sample that finishes much sooner (a small workload run whole) is repeated until about
     min_s, so the rate is not a timing of a fraction of a second."""
     import oracle
     orc = oracle.load()
     threads = cpu_threads()
-    pairs = [(n, h) for n in range(inp.N) for h in range(inp.H)]
-    # a first pair measures the rate; then as many pairs as fit the budget (multiple of threads)
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    f = lambda t: np.ascontiguousarray(t.float().numpy())
+    # rate probe: one (sequence, head) pair on one thread
+    n0 = next(n for n in range(inp.N) if cu[n + 1] > cu[n])
+    s0, e0 = int(cu[n0]), int(cu[n0 + 1])
+    probe = [f(inp.q[s0:e0, :1]), f(inp.k[s0:e0, :1]), f(inp.v[s0:e0, :1]), f(inp.beta[s0:e0, :1])]
     t0 = time.perf_counter()
-    _run_oracle_pairs(orc, inp, pairs[:1], 1)
-    one = time.perf_counter() - t0
-    per_round = max(one, 1e-4)
-    n = int(min(len(pairs), max(threads, (budget_s / per_round) * threads)))
-    if n < len(pairs):
-        n = max(1, (n // threads) * threads)
-    sample = pairs[:n]   # the whole workload when it fits the budget
-    est = per_round * -(-len(sample) // threads)
+    orc.prefill(*probe, z=inp.z[s0:e0, :1].numpy(), A=inp.A[:1].numpy(), n_threads=1,
+                want_state=False)
+    per_tok_head = max(time.perf_counter() - t0, 1e-6) / (e0 - s0)
+    # whole sequences while the estimate stays within the budget (at least one)
+    m = 0
+    est = 0.0
+    while m < inp.N:
+        add = (cu[m + 1] - cu[m]) * inp.H * per_tok_head / threads
+        if m > 0 and est + add > budget_s:
+            break
+        est += add
+        m += 1
+    end = int(cu[m])
+    args = [f(inp.q[:end]), f(inp.k[:end]), f(inp.v[:end]), f(inp.beta[:end])]
+    z = np.ascontiguousarray(inp.z[:end].numpy())
+    A = np.ascontiguousarray(inp.A.numpy())
+    S0 = None if inp.S0 is None else np.ascontiguousarray(inp.S0[:m].numpy())
+    cus = np.ascontiguousarray(cu[:m + 1].astype(np.int32))
     reps = int(min(1000, max(1, min_s // max(est, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps):
-        _run_oracle_pairs(orc, inp, sample, threads)
+        orc.prefill(*args, z=z, A=A, S0=S0, cu_seqlens=cus, n_threads=threads, want_state=False)
     secs = time.perf_counter() - t0
-    tok_heads = reps * sum(inp.lengths[n] for n, _ in sample)
+    tok_heads = reps * end * inp.H
     tokens_per_s = tok_heads / secs / inp.H   # sequence tokens/s over all H heads
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sample)} of {len(pairs)} (sequence, head) pairs of the same workload"
+            "sample": f"the first {m} of {inp.N} sequences, all {inp.H} heads ({m * inp.H} of "
+                      f"{inp.N * inp.H} (sequence, head) pairs, {end} of {inp.total} tokens) of "
+                      f"the same workload"
                       + (f", run {reps} times" if reps > 1 else "")
-                      + f": {tok_heads} token-heads in {secs:.2f} s; fp64 token recurrence"}
+                      + f": {tok_heads} token-heads in {secs:.2f} s; fp64 token recurrence, "
+                        f"inputs converted before timing"}
 
 
-def _run_oracle_pairs(orc, inp, pairs, threads):
-    """Runs the oracle on the given (sequence, head) pairs.  Heads are passed in contiguous
-    batches of bounded host memory, so every batch offers all its pairs to the threads."""
-    f = lambda t: t.float().numpy()
-    per_head = inp.total * inp.dk
-    hb = max(1, min(inp.H, (1 << 26) // max(per_head, 1)))
-    wanted = set(pairs)
-    for h0 in range(0, inp.H, hb):
-        h1 = min(inp.H, h0 + hb)
-        sub = [(n, h - h0) for n, h in pairs if h0 <= h < h1 and (n, h) in wanted]
-        if not sub:
-            continue
-        sl = slice(h0, h1)
-        orc.prefill(f(inp.q[:, sl]), f(inp.k[:, sl]), f(inp.v[:, sl]), f(inp.beta[:, sl]),
-                    z=inp.z[:, sl].numpy(), A=inp.A[sl].numpy(),
-                    S0=None if inp.S0 is None else inp.S0[:, sl].numpy(),
-                    cu_seqlens=inp.cu_seqlens.numpy(), pairs=sub,
-                    n_threads=threads, want_state=False)
+def bench_prefill(name: str, steps: int, warmup: int, checkpoint_interval: int = 0) -> dict:
+    """Times `steps` back-to-back kda_prefill_fwd calls on the named workload, inputs resident
+    in HBM.  Returns the rate over the whole timed region (wall clock, bracketed by device
+    synchronisations), the per-call durations from HIP events recorded between the calls on
+    the launch stream, and the roofline of one call."""
+    import torch
+    from linear_attention_sequence_chunkwise_amd import kda, workloads
+
+    inp = workloads.make(name)
+    dev = lambda t: None if t is None else t.cuda()
+    q, k, v, beta, z, A = map(dev, (inp.q, inp.k, inp.v, inp.beta, inp.z, inp.A))
+    s0 = dev(inp.S0)
+    cu = None if inp.equal_length else dev(inp.cu_seqlens)
+    want_final = name in (workloads.PREFILL_B4, workloads.PREFILL_VARLEN)
+    sN = torch.empty((inp.N, inp.H, inp.dk, inp.dv), dtype=torch.float32, device="cuda") \
+        if want_final else None
+    o = torch.empty((inp.total, inp.H, inp.dv), dtype=q.dtype, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_size(inp.total, inp.N, inp.H, inp.dk, inp.dv, q.dtype),
+                     dtype=torch.uint8, device="cuda")
+
+    ck = ck_off = None
+    if checkpoint_interval > 0:
+        counts = [L // checkpoint_interval for L in inp.lengths]
+        offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        ck = torch.empty((max(1, int(offs[-1])), inp.H, inp.dk, inp.dv), dtype=torch.float32,
+                         device="cuda")
+        ck_off = torch.from_numpy(offs).cuda() if cu is not None else None
+
+    def step():
+        kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=sN,
+                            cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o,
+                            workspace=ws, checkpoints=ck, checkpoint_offsets=ck_off,
+                            checkpoint_interval=checkpoint_interval)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    calls = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])  # ms, per call
+    ms_avg = float(calls.mean())
+    ms_med = float(np.median(calls))
+    ms_per_step = wall * 1e3 / steps
+
+    elem = 2 if inp.dtype == "bf16" else 4
+    fl, by = prefill_algorithmic(inp.dk, inp.dv, elem)
+    tok_heads = inp.total * inp.H
+    state_bytes = (0 if s0 is None else s0.numel() * 4) + (0 if sN is None else sN.numel() * 4) \
+        + (0 if ck is None else ck.numel() * 4)
+    alg_bytes = by * tok_heads + state_bytes
+    achieved = alg_bytes / (ms_avg * 1e-3) / 1e9
+    mfma_tflops = fl * tok_heads / (ms_avg * 1e-3) / 1e12
+    mf = read_mfma(name)
+    if mf is not None:
+        mf["executed_tflops"] = mf["executed_bf16_flops_per_launch"] / (ms_avg * 1e-3) / 1e12
+    warm = inp.total * inp.H * by < 192e6
+    return {
+        "inp": inp,
+        "tokens_per_s": inp.total / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "median_call_ms": ms_med,
+        "config": {"workload": name, "sequences": inp.N, "total_tokens": inp.total,
+                   "heads": inp.H, "dk": inp.dk, "dv": inp.dv, "chunk": CHUNK,
+                   "initial_state": s0 is not None, "final_state": sN is not None,
+                   "workspace_bytes": int(ws.numel()),
+                   "checkpoint_interval": checkpoint_interval or None,
+                   "checkpoint_bytes": 0 if ck is None else int(ck.numel() * 4),
+                   "cache": ("warm: back-to-back calls; inputs, outputs and factor blocks fit "
+                             "the 256 MB last-level cache") if warm else
+                            "back-to-back calls; the working set is many times the 256 MB "
+                            "last-level cache"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(name),
+                     "kernel": "kda_prefill_fwd (one call: chunk table, intra-chunk and "
+                               "state-pass kernels)", "avg_launch_ms": ms_avg,
+                     "median_launch_ms": ms_med, "min_launch_ms": float(calls.min()),
+                     "max_launch_ms": float(calls.max()), "timed_calls": steps,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma_util": {"useful_tflops": mfma_tflops, "peak_tflops": BF16_PEAK_TFLOPS,
+                      "frac": mfma_tflops / BF16_PEAK_TFLOPS,
+                      "useful_flops_per_token_head": fl, "rocprof": mf},
+    }
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None,
+                    help="headline prefill workload (default: the varlen batch of 64 sequences)")
+    ap.add_argument("--extra-workloads", default=None,
+                    help="comma-separated prefill workloads timed after the headline one and "
+                         "reported under 'prefill_other' (default: the batched and the "
+                         "single-sequence workloads; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=256)
@@ -183,6 +280,9 @@ def main():
               "(the (sequence, head) chains would shard across GPUs with no communication, "
               "and each GPU would run this single-GPU path on its share).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     from linear_attention_sequence_chunkwise_amd import kda, workloads
@@ -198,88 +298,36 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    name = args.workload or workloads.PREFILL_B1
-    inp = workloads.make(name)
-    dev = lambda t: None if t is None else t.cuda()
-    q, k, v, beta, z, A = map(dev, (inp.q, inp.k, inp.v, inp.beta, inp.z, inp.A))
-    s0 = dev(inp.S0)
-    cu = None if inp.equal_length else dev(inp.cu_seqlens)
-    want_final = name in (workloads.PREFILL_B4, workloads.PREFILL_VARLEN)
-    sN = torch.empty((inp.N, inp.H, inp.dk, inp.dv), dtype=torch.float32, device="cuda") \
-        if want_final else None
-    o = torch.empty((inp.total, inp.H, inp.dv), dtype=q.dtype, device="cuda")
-    ws = torch.empty(kda.kda_prefill_workspace_size(inp.total, inp.N, inp.H, inp.dk, inp.dv, q.dtype),
-                     dtype=torch.uint8, device="cuda")
-
-    ck = ck_off = None
-    if args.checkpoint_interval > 0:
-        counts = [L // args.checkpoint_interval for L in inp.lengths]
-        offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-        ck = torch.empty((max(1, int(offs[-1])), inp.H, inp.dk, inp.dv), dtype=torch.float32,
-                         device="cuda")
-        ck_off = torch.from_numpy(offs).cuda() if cu is not None else None
-
-    def step():
-        kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=sN,
-                            cu_seqlens=cu, n_seqs=None if cu is not None else inp.N, o=o,
-                            workspace=ws, checkpoints=ck, checkpoint_offsets=ck_off,
-                            checkpoint_interval=args.checkpoint_interval)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_event = ev0.elapsed_time(ev1) / args.steps  # average launch duration on this stream
-    ms_per_step = wall * 1e3 / args.steps
-
-    elem = 2 if inp.dtype == "bf16" else 4
-    fl, by = prefill_algorithmic(inp.dk, inp.dv, elem)
-    tok_heads = inp.total * inp.H
-    state_bytes = (0 if s0 is None else s0.numel() * 4) + (0 if sN is None else sN.numel() * 4) \
-        + (0 if ck is None else ck.numel() * 4)
-    alg_bytes = by * tok_heads + state_bytes
-    achieved = alg_bytes / (ms_event * 1e-3) / 1e9
-    traffic = read_traffic(name)
-    tokens_per_s = inp.total / (ms_per_step * 1e-3)
-    mfma_tflops = fl * tok_heads / (ms_event * 1e-3) / 1e12
+    name = args.workload or workloads.PREFILL_VARLEN
+    head = bench_prefill(name, args.steps, args.warmup, args.checkpoint_interval)
+    inp = head.pop("inp")
+    torch.cuda.empty_cache()
 
     out = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": inp.dtype,
         "data": "synthetic, seeded (q,k ~N(0,1) L2-normalised per head, q/sqrt(dk); v ~N(0,1); "
-                "beta=Sigmoid(N(0,1)); z ~N(0,1); A ~N(0,0.5))",
-        "config": {"workload": name, "sequences": inp.N, "total_tokens": inp.total,
-                   "heads": inp.H, "dk": inp.dk, "dv": inp.dv, "chunk": CHUNK,
-                   "initial_state": s0 is not None, "final_state": sN is not None,
-                   "workspace_bytes": int(ws.numel()),
-                   "checkpoint_interval": args.checkpoint_interval or None,
-                   "checkpoint_bytes": 0 if ck is None else int(ck.numel() * 4),
-                   "cache": "warm: back-to-back calls"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None if traffic is None else traffic,
-                     "kernel": "kda_prefill_fwd (one call: chunk table, intra-chunk and "
-                               "state-pass kernels)", "avg_launch_ms": ms_event,
-                     "algorithmic_bytes_per_launch": alg_bytes},
-        "mfma_util": {"useful_tflops": mfma_tflops, "peak_tflops": BF16_PEAK_TFLOPS,
-                      "frac": mfma_tflops / BF16_PEAK_TFLOPS,
-                      "useful_flops_per_token_head": fl},
+                "beta=Sigmoid(N(0,1)); z ~N(0,1); A ~N(0,0.5)"
+                + ("; initial states ~N(0,0.02)" if inp.S0 is not None else "") + ")",
+        "config": head["config"],
+        "median_call_ms": head["median_call_ms"],
+        "roofline": head["roofline"],
+        "mfma_util": head["mfma_util"],
     }
 
-    mf = read_mfma(name)
-    if mf is not None:
-        mf["executed_tflops"] = mf["executed_bf16_flops_per_launch"] / (ms_event * 1e-3) / 1e12
-    out["mfma_util"]["rocprof"] = mf
+    extra = args.extra_workloads
+    if extra is None:
+        extra = ",".join(w for w in (workloads.PREFILL_B4, workloads.PREFILL_B1) if w != name)
+    others = {}
+    for w in [x for x in extra.split(",") if x and x != "none"]:
+        r = bench_prefill(w, args.steps, args.warmup)
+        r.pop("inp")
+        torch.cuda.empty_cache()
+        others[w] = r
+    if others:
+        out["prefill_other"] = others
 
     if not args.no_decode:
         out["decode"] = bench_decode(args.decode_steps)

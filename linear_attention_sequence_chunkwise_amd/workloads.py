@@ -6,6 +6,9 @@ CPU oracle consume what it produces, so the two sides see bit-identical inputs.
 
 Recipe (numpy PCG64 ``default_rng(seed)``, float32 draws, fixed draw order):
   lengths (varlen only) -> q -> k -> v -> beta -> z -> A -> S0
+  Each tensor after the lengths is cut, along its leading axes, into blocks of about 4M
+  elements; block b is drawn from the b-th PCG64 stream spawned from the generator (streams
+  spawned in draw order), so the values do not depend on how many host threads draw them.
   * q, k ~ N(0, 1), each (token, head) vector L2-normalised over d_k in fp32; q then scaled
     by 1/sqrt(d_k).  (The KDA input branch normalises q and k per head; the scale is the
     usual attention scale, applied here because o = S^T q carries none.)
@@ -19,8 +22,10 @@ Recipe (numpy PCG64 ``default_rng(seed)``, float32 draws, fixed draw order):
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional
 
 import numpy as np
 import torch
@@ -28,19 +33,60 @@ import torch
 _DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
 
-def _normal(rng: np.random.Generator, shape, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    if mean != 0.0:
-        x += np.float32(mean)
-    return x
+_BLOCK_ELEMS = 1 << 22   # elements per independently seeded block (fixed: part of the recipe)
+_pool: Optional[ThreadPoolExecutor] = None
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal(rng: np.random.Generator, shape, mean: float = 0.0, std: float = 1.0,
+            post: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> np.ndarray:
+    """float32 N(mean, std) draws of `shape`, block by block (see the recipe); `post` maps
+    each block of whole last-axis rows (applied after the scale and shift)."""
+    shape = tuple(int(x) for x in shape)
+    last = shape[-1]
+    rows = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
+    out = np.empty((rows, last), dtype=np.float32)
+    brows = max(1, _BLOCK_ELEMS // max(last, 1))
+    nblk = max(1, -(-rows // brows))
+    streams = rng.spawn(nblk)
+
+    def fill(b):
+        r0, r1 = b * brows, min(rows, (b + 1) * brows)
+        if r1 <= r0:
+            return
+        x = streams[b].standard_normal(size=(r1 - r0, last), dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        if mean != 0.0:
+            x += np.float32(mean)
+        out[r0:r1] = post(x) if post is not None else x
+
+    global _pool
+    if nblk == 1:
+        fill(0)
+    else:
+        if _pool is None:
+            _pool = ThreadPoolExecutor(max_workers=_threads())
+        list(_pool.map(fill, range(nblk)))
+    return out.reshape(shape)
 
 
 def _l2norm_lastdim(x: np.ndarray) -> np.ndarray:
     n = np.sqrt(np.einsum("...d,...d->...", x, x, dtype=np.float32))
     n = np.maximum(n, np.float32(1e-12))
     return x / n[..., None]
+
+
+def _l2norm_scaled(scale: float):
+    s = np.float32(scale)
+    return lambda x: _l2norm_lastdim(x) * s
 
 
 def _sigmoid_f32(x: np.ndarray) -> np.ndarray:
@@ -106,10 +152,10 @@ def prefill_inputs(lengths: List[int], H: int, dk: int, dv: int, dtype: str, see
                    rng: Optional[np.random.Generator] = None) -> PrefillInputs:
     rng = rng if rng is not None else np.random.default_rng(seed)
     total = int(sum(lengths))
-    q = _l2norm_lastdim(_normal(rng, (total, H, dk))) * np.float32(1.0 / math.sqrt(dk))
-    k = _l2norm_lastdim(_normal(rng, (total, H, dk)))
+    q = _normal(rng, (total, H, dk), post=_l2norm_scaled(1.0 / math.sqrt(dk)))
+    k = _normal(rng, (total, H, dk), post=_l2norm_lastdim)
     v = _normal(rng, (total, H, dv))
-    beta = _sigmoid_f32(_normal(rng, (total, H)))
+    beta = _normal(rng, (total, H), post=_sigmoid_f32)
     z = _normal(rng, (total, H, dk), z_mean, z_std)
     A = _normal(rng, (H, dk), 0.0, 0.5)
     S0 = _normal(rng, (len(lengths), H, dk, dv), 0.0, s0_std) if s0_std is not None else None
@@ -172,10 +218,10 @@ def decode_inputs(N: int, H: int, dk: int, dv: int, steps: int, dtype: str, seed
                   name: str = "custom") -> DecodeInputs:
     """Draw order: q, k, v, beta, z (all steps at once), A, S0."""
     rng = np.random.default_rng(seed)
-    q = _l2norm_lastdim(_normal(rng, (steps, N, H, dk))) * np.float32(1.0 / math.sqrt(dk))
-    k = _l2norm_lastdim(_normal(rng, (steps, N, H, dk)))
+    q = _normal(rng, (steps, N, H, dk), post=_l2norm_scaled(1.0 / math.sqrt(dk)))
+    k = _normal(rng, (steps, N, H, dk), post=_l2norm_lastdim)
     v = _normal(rng, (steps, N, H, dv))
-    beta = _sigmoid_f32(_normal(rng, (steps, N, H)))
+    beta = _normal(rng, (steps, N, H), post=_sigmoid_f32)
     z = _normal(rng, (steps, N, H, dk), z_mean, z_std)
     A = _normal(rng, (H, dk), 0.0, 0.5)
     S0 = _normal(rng, (N, H, dk, dv), 0.0, s0_std)

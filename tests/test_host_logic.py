@@ -54,6 +54,21 @@ def test_bf16_inputs_round_the_fp32_draws_to_nearest_even():
     assert torch.equal(f.z, h.z)  # the gate input stays fp32
 
 
+def test_blocked_draws_do_not_depend_on_threads(monkeypatch):
+    """Each block of rows comes from its own stream spawned in order from the generator, so
+    the thread pool that fills them changes nothing: the draws equal a serial fill."""
+    monkeypatch.setattr(workloads, "_BLOCK_ELEMS", 256)
+    got = workloads._normal(np.random.default_rng(77), (37, 5, 64), -4.0, 2.0,
+                            post=workloads._l2norm_lastdim)
+    streams = np.random.default_rng(77).spawn(-(-37 * 5 // 4))  # 4 rows of 64 per block
+    rows = []
+    for s in streams:
+        x = s.standard_normal(size=(4, 64), dtype=np.float32) * np.float32(2.0) + np.float32(-4.0)
+        rows.append(workloads._l2norm_lastdim(x))
+    want = np.concatenate(rows)[:37 * 5].reshape(37, 5, 64)
+    assert np.array_equal(got, want)
+
+
 def test_varlen_lengths_are_log_uniform_in_range():
     rng = np.random.default_rng(3)
     lens = workloads.varlen_lengths(rng, 2000, 512, 16384)
