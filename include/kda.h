@@ -15,7 +15,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
- *     allocates, frees or keeps device memory, and keeps no state between calls.
+ *     allocates or frees device memory and keeps no state between calls.  The one
+ *     exception is the fixed scratch array of kda_prefill_fwd_noalloc, a static device
+ *     variable that each device holds from the library's load until the process ends.
  *   - Layouts are row-major with the last dimension contiguous:
  *       q, k, z  [tokens, H, dk]      v, o  [tokens, H, dv]      beta  [tokens, H]
  *       A        [H, dk]              states [N, H, dk, dv] (dv fastest, rows = key channels)
@@ -51,7 +53,9 @@ typedef enum kda_status {
     KDA_ERR_UNSUPPORTED = -3, /* head size, element type or g_min outside what is compiled  */
     KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                           */
     KDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kda_prefill_workspace_size */
-    KDA_ERR_HIP = -6          /* the HIP runtime rejected a launch                          */
+    KDA_ERR_HIP = -6,         /* the HIP runtime rejected a launch                          */
+    KDA_ERR_SCRATCH = -7      /* kda_prefill_fwd_noalloc: the call needs more than          */
+                              /* KDA_NOALLOC_SCRATCH_BYTES of scratch                       */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -137,6 +141,31 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
                            const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
                            int dk, int dv, void* o, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * kda_prefill_fwd_noalloc -- kda_prefill_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the workspace taken from a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES per device instead of a caller buffer.
+ *
+ * All arguments of kda_prefill_fwd keep their meaning; there is no workspace argument.
+ *   - The call is accepted only when kda_prefill_workspace_size(...) of the same sizes is at
+ *     most KDA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 4096 tokens x 16 heads at d = 128, or
+ *     about 1,100 (chunk, head) pairs); KDA_ERR_SCRATCH otherwise, checked on the host
+ *     before anything else happens.
+ *   - The array's device address is looked up once per device (hipGetSymbolAddress, on the
+ *     first call with that device current); a failed lookup returns KDA_ERR_HIP.  The call
+ *     itself allocates nothing (no hipMalloc, no library allocation).
+ *   - Every call on a device shares that device's array and leaves its contents undefined:
+ *     calls that overlap in time on one device (several streams, several host threads)
+ *     race on it and must be ordered by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_prefill_fwd_noalloc(kda_dtype dt, const void* q, const void* k, const void* v,
+                                   const void* beta, const float* z, const float* A,
+                                   float g_min, const float* initial_state, float* final_state,
+                                   const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total,
+                                   int H, int dk, int dv, void* o, hipStream_t stream);
 
 /*
  * kda_prefill_fwd_checkpointed -- kda_prefill_fwd that also writes prefix-cache checkpoints:

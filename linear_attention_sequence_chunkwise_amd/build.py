@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_prefill_split.hip", "kda_decode.hip", "kda_epilogue.hip", "kda_prologue.hip"]
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_prefill_split.hip", "kda_decode.hip", "kda_epilogue.hip",
+           "kda_prologue.hip", "kda_noalloc.hip"]
 ARCH = "gfx950"
 
 

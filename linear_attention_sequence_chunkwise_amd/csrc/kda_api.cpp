@@ -2,7 +2,8 @@
 //
 // Every check runs on the host before any HIP call, so an invalid call launches nothing
 // and writes nothing.  The library allocates nothing and keeps no state between calls
-// except a per-device cache of the compute-unit count used to size launches.
+// except a per-device cache of the compute-unit count used to size launches and, for
+// kda_prefill_fwd_noalloc, the per-device address of its static scratch array.
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
@@ -55,6 +56,8 @@ const char* kda_status_str(kda_status s) {
         case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+        case KDA_ERR_SCRATCH:
+            return "KDA_ERR_SCRATCH: the call needs more than KDA_NOALLOC_SCRATCH_BYTES of scratch";
     }
     return "unknown kda_status";
 }
@@ -103,12 +106,17 @@ struct Checkpoints {
     int interval;            // tokens, a positive multiple of 64
 };
 
+// Where the workspace comes from: the caller's buffer, or the device's static scratch array
+// (kda_prefill_fwd_noalloc).
+enum class WorkspaceSource { kCaller, kStaticScratch };
+
 kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* v,
                         const void* beta, const float* z, const float* A, float g_min,
                         const float* initial_state, float* final_state,
                         const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total, int H,
                         int dk, int dv, void* o, const Checkpoints& ck, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, hipStream_t stream,
+                        WorkspaceSource wsrc = WorkspaceSource::kCaller) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (n_seqs <= 0 || T_or_total < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     const int64_t total = cu_seqlens ? T_or_total : static_cast<int64_t>(n_seqs) * T_or_total;
@@ -140,8 +148,14 @@ kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* 
         if (!aligned16(ck.states) || (ck.offsets && (reinterpret_cast<uintptr_t>(ck.offsets) & 3u)))
             return KDA_ERR_ALIGN;
     }
-    if (total == 0 && !final_state) return KDA_OK;  // nothing to compute or write
     const size_t need = kda_prefill_workspace_size(total, n_seqs, H, dk, dv, dt);
+    if (wsrc == WorkspaceSource::kStaticScratch && need > KDA_NOALLOC_SCRATCH_BYTES)
+        return KDA_ERR_SCRATCH;
+    if (total == 0 && !final_state) return KDA_OK;  // nothing to compute or write
+    if (wsrc == WorkspaceSource::kStaticScratch) {
+        if (kda::noalloc_scratch(&workspace) != hipSuccess) return KDA_ERR_HIP;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
 
     kda::SplitArgs a{};
@@ -181,6 +195,16 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
     return prefill_impl(dt, q, k, v, beta, z, A, g_min, initial_state, final_state, cu_seqlens,
                         n_seqs, T_or_total, H, dk, dv, o, Checkpoints{nullptr, nullptr, 0},
                         workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_fwd_noalloc(kda_dtype dt, const void* q, const void* k, const void* v,
+                                   const void* beta, const float* z, const float* A,
+                                   float g_min, const float* initial_state, float* final_state,
+                                   const int32_t* cu_seqlens, int n_seqs, int64_t T_or_total,
+                                   int H, int dk, int dv, void* o, hipStream_t stream) {
+    return prefill_impl(dt, q, k, v, beta, z, A, g_min, initial_state, final_state, cu_seqlens,
+                        n_seqs, T_or_total, H, dk, dv, o, Checkpoints{nullptr, nullptr, 0},
+                        nullptr, 0, stream, WorkspaceSource::kStaticScratch);
 }
 
 kda_status kda_prefill_fwd_checkpointed(kda_dtype dt, const void* q, const void* k,

@@ -113,6 +113,10 @@ struct ShortConvArgs {
     void* y;                // [total, C]
 };
 
+// Device address of the calling thread's current device's static scratch array
+// (KDA_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
 hipError_t launch_short_conv(const ShortConvArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_output_gate(const OutputGateArgs& a, int dv, bool bf16, hipStream_t stream);

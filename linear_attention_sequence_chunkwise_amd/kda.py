@@ -21,9 +21,12 @@ G_MIN = -5.0
 
 # exported symbols, in the order include/kda.h declares them
 SYMBOLS = ("kda_gate", "kda_prefill_workspace_size", "kda_prefill_fwd",
-           "kda_prefill_fwd_checkpointed", "kda_decode_step", "kda_decode_verify",
-           "kda_decode_commit", "kda_output_gate", "kda_short_conv", "kda_status_str")
+           "kda_prefill_fwd_noalloc", "kda_prefill_fwd_checkpointed", "kda_decode_step",
+           "kda_decode_verify", "kda_decode_commit", "kda_output_gate", "kda_short_conv",
+           "kda_status_str")
 MAX_DRAFT = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
+KDA_ERR_SCRATCH = -7
 
 _lib = None
 
@@ -53,6 +56,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prefill_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32,
                                     i32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_fwd.restype = i32
+    lib.kda_prefill_fwd_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32,
+                                            i64, i32, i32, i32, vp, vp]
+    lib.kda_prefill_fwd_noalloc.restype = i32
     lib.kda_prefill_fwd_checkpointed.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32,
                                                  i64, i32, i32, i32, vp, vp, vp, i32, vp,
                                                  ctypes.c_size_t, vp]
@@ -216,6 +222,43 @@ def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=Non
         dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min, _ptr(initial_state),
         _ptr(final_state), _ptr(cu_seqlens), N, T_or_total, H, dk, dv, _ptr(o), _ptr(workspace),
         wbytes, _stream(stream)))
+    return o
+
+
+def kda_prefill_fwd_noalloc(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=None,
+                            final_state=None, cu_seqlens=None, n_seqs: Optional[int] = None,
+                            o=None, stream=None):
+    """kda_prefill_fwd with its workspace in the library's static per-device scratch array
+    (at most NOALLOC_SCRATCH_BYTES; larger problems raise KDAError with KDA_ERR_SCRATCH).
+    Allocates nothing when `o` is given.  Calls that overlap on one device race."""
+    lib = load_library()
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        T_or_total = total
+    else:
+        N = 1 if n_seqs is None else int(n_seqs)
+        if total % N:
+            raise ValueError("total tokens not divisible by n_seqs")
+        T_or_total = total // N
+    if o is None:
+        o = torch.empty((total, H, dv), dtype=q.dtype, device=q.device)
+    et, f32 = q.dtype, torch.float32
+    _expect("k", k, (total, H, dk), et)
+    _expect("v", v, (total, H, dv), et)
+    _expect("beta", beta, (total, H), et)
+    _expect("z", z, (total, H, dk), f32)
+    _expect("A", A, (H, dk), f32)
+    _expect("initial_state", initial_state, (N, H, dk, dv), f32)
+    _expect("final_state", final_state, (N, H, dk, dv), f32)
+    _expect("cu_seqlens", cu_seqlens, (N + 1,), torch.int32)
+    _expect("o", o, (total, H, dv), et)
+    _dev(q, k, v, beta, z, A, initial_state, final_state, cu_seqlens, o)
+    _check("kda_prefill_fwd_noalloc", lib.kda_prefill_fwd_noalloc(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), g_min,
+        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N, T_or_total, H, dk, dv,
+        _ptr(o), _stream(stream)))
     return o
 
 

@@ -14,7 +14,7 @@ from linear_attention_sequence_chunkwise_amd import kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
 P = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: validation fails first
 MIS = ctypes.c_void_p(0x10004)  # misaligned
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, ESCRATCH):
         s = kda.status_str(code)
         assert s.startswith("KDA_"), s
     assert "unknown" in kda.status_str(42)
@@ -75,6 +75,34 @@ def test_prefill_rejects_bad_arguments(lib):
     assert prefill(lib, T=1 << 45, N=1 << 10) == ESHAPE
     # (chunk slots) x heads intra-chunk workgroups must fit one 1-D grid
     assert prefill(lib, H=65535, T=64 * 40000) == ESHAPE
+
+
+def test_noalloc_prefill_scratch_limit(lib):
+    """The allocation-free prefill states its scratch limit in the header, rejects a call
+    whose workspace would exceed it on the host (before any HIP call, so this runs without a
+    GPU), and applies the ordinary argument checks first."""
+    src = open(HEADER).read()
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_SCRATCH_BYTES
+    assert kda.KDA_ERR_SCRATCH == ESCRATCH
+
+    def call(T, H=16, dk=128, N=1, dt=BF16, A=P):
+        return lib.kda_prefill_fwd_noalloc(dt, P, P, P, P, P, A, -5.0, None, None, None, N, T,
+                                           H, dk, dk, P, None)
+
+    # a 4096-token, 16-head d = 128 call fits; 512 more tokens do not
+    fits = lib.kda_prefill_workspace_size(4096, 1, 16, 128, 128, BF16)
+    assert fits <= kda.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_prefill_workspace_size(4096 + 512, 1, 16, 128, 128, BF16) > kda.NOALLOC_SCRATCH_BYTES
+    assert call(4096 + 512) == ESCRATCH
+    assert call(1 << 20, H=32) == ESCRATCH
+    # ordinary checks come first
+    assert call(64, dt=7) == EUNSUP
+    assert call(64, A=None) == ENULL
+    assert call(64, dk=96) == EUNSUP
+    # nothing to compute and nothing to write: accepted without touching the device
+    assert lib.kda_prefill_fwd_noalloc(BF16, None, None, None, None, None, P, -5.0, None, None,
+                                       None, 1, 0, 2, 128, 128, None, None) == OK
 
 
 def test_checkpointed_prefill_rejects_bad_arguments(lib):
