@@ -181,6 +181,9 @@ kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* 
     const int64_t np = a.npairs;
     int ncw = 4;
     while (ncw > 1 && np * (dk / (8 * ncw)) <= cus) ncw /= 2;
+    // With a chain for every compute unit, one fused workgroup per (sequence, head) keeps the
+    // factor blocks on chip (bf16 inputs; the fp32 form needs more registers than it has).
+    if (dt == KDA_BF16 && np >= cus) ncw = 0;
     return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ncw, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

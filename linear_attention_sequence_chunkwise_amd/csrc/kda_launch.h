@@ -44,7 +44,8 @@ struct PrefillArgs {
 // holding the varlen chunk table and one factor block per (chunk, head).
 struct SplitArgs : PrefillArgs {
     int64_t total;           // packed token count
-    int32_t* chunk_start;    // [n_seqs + 1] in the workspace (varlen only)
+    int32_t* chunk_start;    // [n_seqs + 1] in the workspace (varlen only); the fused kernel
+                             // keeps its chain order there instead
     void* blocks;            // factor blocks in the workspace
     float* ckpt;             // nullable: states at every ckpt_chunks-th chunk boundary
     const int32_t* ckpt_off; // [n_seqs + 1] first checkpoint of each sequence (varlen)
@@ -55,7 +56,8 @@ struct SplitArgs : PrefillArgs {
 size_t split_block_bytes(int dk);
 int64_t split_max_chunks(int64_t total, int n_seqs);
 size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk);
-// State-pass workgroup shape: ncw (1, 2 or 4) compute waves of 16 dv columns each.
+// State-pass workgroup shape: ncw (1, 2 or 4) compute waves of 16 dv columns each, or 0 for
+// the fused single-kernel prefill (one eight-wave workgroup per (sequence, head)).
 hipError_t launch_prefill_split(const SplitArgs& a, int dk, bool bf16, int ncw, hipStream_t stream);
 
 struct DecodeArgs {

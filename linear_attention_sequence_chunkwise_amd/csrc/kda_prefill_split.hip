@@ -157,6 +157,38 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* cu, in
     if (tid == 0) chunk_start[0] = 0;
 }
 
+// ---- chain order for the fused prefill: sequences by decreasing chunk count ---------------
+// The fused kernel runs one workgroup per (sequence, head) chain, so a batch of chains of
+// mixed lengths finishes sooner when the longest start first.  One workgroup counting-sorts
+// the sequences into buckets of their chunk count (floor(log2) and the next two bits: about
+// 19% apart), longest bucket first.  The order within a bucket is arbitrary: chains are
+// independent, so it affects only when each one runs, never a result.
+constexpr int kOrderBuckets = 128;
+__device__ __forceinline__ int chain_bucket(const int32_t* cu, int n) {
+    const uint32_t c = static_cast<uint32_t>((cu[n + 1] - cu[n] + kC - 1) / kC);
+    if (c == 0) return 0;
+    const int e = 31 - __builtin_clz(c);
+    return 1 + 4 * e + static_cast<int>(((static_cast<uint64_t>(c) << 2) >> e) & 3u);
+}
+__global__ void __launch_bounds__(1024) chain_order_kernel(const int32_t* cu, int n_seqs, int32_t* order) {
+    __shared__ int32_t cnt[kOrderBuckets];
+    const int tid = threadIdx.x;
+    if (tid < kOrderBuckets) cnt[tid] = 0;
+    __syncthreads();
+    for (int n = tid; n < n_seqs; n += 1024) atomicAdd(&cnt[chain_bucket(cu, n)], 1);
+    __syncthreads();
+    if (tid == 0) {  // exclusive prefix over the buckets, longest first
+        int run = 0;
+        for (int b = kOrderBuckets - 1; b >= 0; --b) {
+            const int k = cnt[b];
+            cnt[b] = run;
+            run += k;
+        }
+    }
+    __syncthreads();
+    for (int n = tid; n < n_seqs; n += 1024) order[atomicAdd(&cnt[chain_bucket(cu, n)], 1)] = n;
+}
+
 // ---- K1: intra-chunk factors ------------------------------------------------------------
 // One workgroup of four waves per (chunk, head).  Wave w owns 16-token tile w and works in
 // the MFMA operand layout from the start: lane (g, li) holds token 16w + li and the channels
@@ -209,61 +241,65 @@ __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
     return __uint_as_float(i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w);
 }
 
+// One (chunk, head) of intra-chunk work, phase by phase, for a group of four waves (wave w
+// owns 16-token tile w).  The phases are separated by workgroup barriers, which the caller
+// places: the intra-chunk kernel runs them back to back, the fused kernel interleaves them
+// with its state-pass waves.  Lane (g, li) of wave w holds token 16w + li and the channels
+// 32s + 8g .. 32s + 8g + 7 for every K-step s, exactly the 16 bytes per step it feeds to a
+// 16x16x32 product.  The cumulative decays within a tile are therefore an inclusive scan of
+// log-decays across the 16 lanes of a DPP row, K~ and Q~ leave registers as linear 1 KiB
+// lane-order writes, and only the column operands (read by other waves) and K^n (transposed
+// for the state pass) go through LDS.
+//   load     q, k, z rows into registers (rows past the end read 0), raw beta
+//   phase 1  beta -> LDS
+//   phase 2  gates, tile-local scans, F = e^{Gamma_i - rho_w}; tile totals -> LDS
+//   phase 3  per-channel products of tile totals; e^{Gamma_n} -> block
+//   phase 4  operands: K~, Q~ -> block, column operand and K^n staging -> LDS
+//   phase 5  K^n^T -> block in lane order
+//   phase 6  the 10 lower 16x16 tiles of A_kk and A_qk
+//   phase 7  diagonal blocks of T (wave 3)
+//   phase 8  off-diagonal blocks of T (waves 0-2)
+//   phase 9  M = A_qk T
+// The block (K~, Q~, K^n^T, e^{Gamma_n}) is written through `blk`: global memory for the
+// intra-chunk kernel, an LDS stage for the fused kernel.  T and M go to the LDS arrays Tb and
+// Mb (the fused kernel's stage, or staging that the intra-chunk kernel copies out).
 template <int DK, typename TIn>
-__global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_kernel(SplitArgs args) {
+struct Producer {
     using Smem = IntraSmem<DK>;
-    // four workgroups per CU (bf16 inputs, see the launch bounds) need their LDS to fit 160 KiB
-    static_assert(sizeof(Smem) * (sizeof(TIn) == 2 ? 4 : 2) <= 160 * 1024, "intra-chunk LDS budget");
     using P = Pair<TIn>;
     using B = Block<DK>;
-    constexpr int NT = 256;
-    constexpr int KS = DK / 32;
-    constexpr int MT = DK / 16;
-    constexpr int ES = static_cast<int>(sizeof(TIn));
+    static constexpr int KS = DK / 32;
+    static constexpr int MT = DK / 16;
+    static constexpr int ES = static_cast<int>(sizeof(TIn));
 
-    __shared__ Smem sm;
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-
-    // workgroup -> (chunk slot, head), the head fastest: the workgroups in flight together
-    // read the same tokens' rows of every head, which lie next to each other in memory
-    const int H = args.H, slot = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
-    // chunk slot -> (sequence, chunk of the sequence)
-    int n;
-    int64_t tok0, len, c0;
-    if (args.cu) {
-        if (slot >= args.chunk_start[args.n_seqs]) return;
-        n = slot_seq(args.chunk_start, args.n_seqs, slot);
-        tok0 = args.cu[n];
-        len = static_cast<int64_t>(args.cu[n + 1]) - tok0;
-        c0 = static_cast<int64_t>(slot - args.chunk_start[n]) * kC;
-    } else {
-        const int nc = static_cast<int>((args.T + kC - 1) / kC);
-        n = slot / nc;
-        if (n >= args.n_seqs) return;
-        tok0 = static_cast<int64_t>(n) * args.T;
-        len = args.T;
-        c0 = static_cast<int64_t>(slot - n * nc) * kC;
-    }
-    const int clen = static_cast<int>(len - c0 < kC ? len - c0 : kC);
-    const int64_t t0 = tok0 + c0;
-    char* blk = static_cast<char*>(args.blocks) + (static_cast<size_t>(slot) * H + h) * B::BYTES;
-
-    const uint32_t rowK = static_cast<uint32_t>(H) * DK * ES;
-    const uint32_t rowZ = static_cast<uint32_t>(H) * DK * 4;
-    const uint32_t rowB = static_cast<uint32_t>(H) * ES;
-    const char* kbase = static_cast<const char*>(args.k) + static_cast<size_t>(h) * DK * ES;
-    const char* qbase = static_cast<const char*>(args.q) + static_cast<size_t>(h) * DK * ES;
-    const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
-    const char* zbase = reinterpret_cast<const char*>(args.z) + static_cast<size_t>(h) * DK * 4;
-    const float gscale = args.g_min * kLog2e;
-
-    // ---- loads: this lane's token r and channels 32s + 8g .. (rows past the end read 0) ----
-    const int r = 16 * w + li;
+    int tid, w, lane, g, li, r;
+    int clen;
     typename P::Row8 pk[KS], pq[KS];
     uint4 pz[KS][2];
-    {
+    uint32_t rbeta;
+    float F[KS][8];
+    uint4 kr[KS], qr[KS];
+
+    __device__ __forceinline__ void init(int thread) {
+        tid = thread;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        lane = tid & 63;
+        g = lane >> 4;
+        li = lane & 15;
+        r = 16 * w + li;
+    }
+
+    // loads of the chunk of `n_valid` tokens starting at token t0 of head h
+    __device__ __forceinline__ void load(const SplitArgs& args, int h, int64_t t0, int n_valid) {
+        clen = n_valid;
+        const int H = args.H;
+        const uint32_t rowK = static_cast<uint32_t>(H) * DK * ES;
+        const uint32_t rowZ = static_cast<uint32_t>(H) * DK * 4;
+        const uint32_t rowB = static_cast<uint32_t>(H) * ES;
+        const char* kbase = static_cast<const char*>(args.k) + static_cast<size_t>(h) * DK * ES;
+        const char* qbase = static_cast<const char*>(args.q) + static_cast<size_t>(h) * DK * ES;
+        const char* bbase = static_cast<const char*>(args.beta) + static_cast<size_t>(h) * ES;
+        const char* zbase = reinterpret_cast<const char*>(args.z) + static_cast<size_t>(h) * DK * 4;
         const rsrc_t rk = make_rsrc(kbase + t0 * rowK, clen * rowK);
         const rsrc_t rq = make_rsrc(qbase + t0 * rowK, clen * rowK);
         const rsrc_t rz = make_rsrc(zbase + t0 * rowZ, clen * rowZ);
@@ -275,20 +311,22 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
             pz[s][0] = bload16(rz, r * rowZ + ch * 4);
             pz[s][1] = bload16(rz, r * rowZ + ch * 4 + 16);
         }
-        if (tid < DK) sm.ae[tid] = -expf(args.A[h * DK + tid]) * kLog2e;
         if (tid < kC) {
             const rsrc_t rb = make_rsrc(bbase + t0 * rowB, clen * rowB);
-            sm.beta[tid] = P::load_beta(rb, tid * rowB);
+            if constexpr (sizeof(TIn) == 2) rbeta = bload2(rb, tid * rowB);
+            else rbeta = bload4(rb, tid * rowB);
         }
     }
-    lds_barrier();
 
-    // ---- gates, then F = e^{Gamma_i - rho_w}: log2 alpha = g log2(e) (tokens past the end: 0),
+    __device__ __forceinline__ void phase1(float* beta) {
+        if (tid < kC) beta[tid] = __uint_as_float(sizeof(TIn) == 2 ? rbeta << 16 : rbeta);
+    }
+
+    // gates, then F = e^{Gamma_i - rho_w}: log2 alpha = g log2(e) (tokens past the end: 0),
     // an inclusive sum over the 16 tokens of the tile (lanes li of one row; a lane with no
     // source adds 0), then one exp2.  The tile-local sum lies in [-80 log2(e), 0], the
-    // pages' 16-token bound, so the exponential is finite and normal in fp32. ----------------
-    float F[KS][8];
-    {
+    // pages' 16-token bound, so the exponential is finite and normal in fp32.
+    __device__ __forceinline__ void phase2(Smem& sm, float gscale) {
         const bool valid = r < clen;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -325,103 +363,104 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
             }
         }
     }
-    lds_barrier();
 
-    // ---- per-channel products of tile decays, once per workgroup: every wave reads its own
+    // per-channel products of tile decays, once per (chunk, head): every wave reads its own
     // row, so no lane selects tiles by the wave index.  e^{Gamma_n} goes to the block.
-    if (tid < DK) {
-        const float t0 = sm.ttile[0][tid], t1 = sm.ttile[1][tid], t2 = sm.ttile[2][tid], t3 = sm.ttile[3][tid];
-        const float p2 = t0 * t1, p3 = p2 * t2, s12 = t1 * t2;
-        sm.pre[0][tid] = 1.f;
-        sm.pre[1][tid] = t0;
-        sm.pre[2][tid] = p2;
-        sm.pre[3][tid] = p3;
-        sm.suf[0][tid] = s12 * t3;
-        sm.suf[1][tid] = t2 * t3;
-        sm.suf[2][tid] = t3;
-        sm.suf[3][tid] = 1.f;
-        reinterpret_cast<float*>(blk + B::DN)[tid] = p3 * t3;
-    }
-    lds_barrier();
-
-    // ---- operands.  Row operands (registers): Kr = k e^{Gamma_i - rho_w}, Qr likewise.
-    // Column operand (LDS): k e^{rho_{w+1} - Gamma_i}.  Factor block: K~ = k e^{Gamma_i},
-    // Q~ = q e^{Gamma_i} (lane order, straight from registers), K^n staged for transposition.
-    uint4 kr[KS], qr[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int ch = 32 * s + 8 * g;
-        // two halves of the lane's eight channels (fewer values live at once)
-        uint32_t pkr[4], pqr[4], pkc[4], pkt[4], pqt[4], pkn[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            // e^{rho_{w+1} - rho_w}, e^{rho_w} and e^{Gamma_n - rho_{w+1}} of the four channels
-            const float4 tw4 = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4 * hh]);
-            const float4 eR4 = *reinterpret_cast<const float4*>(&sm.pre[w][ch + 4 * hh]);
-            const float4 eN4 = *reinterpret_cast<const float4*>(&sm.suf[w][ch + 4 * hh]);
-            const float tws[4] = {tw4.x, tw4.y, tw4.z, tw4.w};
-            const float eRs[4] = {eR4.x, eR4.y, eR4.z, eR4.w};
-            const float eNs[4] = {eN4.x, eN4.y, eN4.z, eN4.w};
-            float vkr[4], vqr[4], vkc[4], vkt[4], vqt[4], vkn[4];
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int e = 4 * hh + e4;
-                const float tw = tws[e4], eR = eRs[e4], eN = eNs[e4];
-                const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
-                const float f = F[s][e];
-                const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
-                vkr[e4] = kf * f;
-                vqr[e4] = qf * f;
-                vkc[e4] = kf * E;
-                vkt[e4] = vkr[e4] * eR;
-                vqt[e4] = vqr[e4] * eR;
-                vkn[e4] = vkc[e4] * eN;
-            }
-#pragma unroll
-            for (int p2 = 0; p2 < 2; ++p2) {
-                pkr[2 * hh + p2] = pack_bf16x2(vkr[2 * p2], vkr[2 * p2 + 1]);
-                pqr[2 * hh + p2] = pack_bf16x2(vqr[2 * p2], vqr[2 * p2 + 1]);
-                pkc[2 * hh + p2] = pack_bf16x2(vkc[2 * p2], vkc[2 * p2 + 1]);
-                pkt[2 * hh + p2] = pack_bf16x2(vkt[2 * p2], vkt[2 * p2 + 1]);
-                pqt[2 * hh + p2] = pack_bf16x2(vqt[2 * p2], vqt[2 * p2 + 1]);
-                pkn[2 * hh + p2] = pack_bf16x2(vkn[2 * p2], vkn[2 * p2 + 1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+    __device__ __forceinline__ void phase3(Smem& sm, char* blk) {
+        if (tid < DK) {
+            const float t0 = sm.ttile[0][tid], t1 = sm.ttile[1][tid], t2 = sm.ttile[2][tid], t3 = sm.ttile[3][tid];
+            const float p2 = t0 * t1, p3 = p2 * t2, s12 = t1 * t2;
+            sm.pre[0][tid] = 1.f;
+            sm.pre[1][tid] = t0;
+            sm.pre[2][tid] = p2;
+            sm.pre[3][tid] = p3;
+            sm.suf[0][tid] = s12 * t3;
+            sm.suf[1][tid] = t2 * t3;
+            sm.suf[2][tid] = t3;
+            sm.suf[3][tid] = 1.f;
+            reinterpret_cast<float*>(blk + B::DN)[tid] = p3 * t3;
         }
-        kr[s] = make_uint4(pkr[0], pkr[1], pkr[2], pkr[3]);
-        qr[s] = make_uint4(pqr[0], pqr[1], pqr[2], pqr[3]);
-        const int piece = (w * KS + s) * 64 + lane;
-        sm.b.kc[piece] = make_uint4(pkc[0], pkc[1], pkc[2], pkc[3]);
-        *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) = make_uint4(pkt[0], pkt[1], pkt[2], pkt[3]);
-        *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) = make_uint4(pqt[0], pqt[1], pqt[2], pqt[3]);
-        *reinterpret_cast<uint4*>(&sm.a.kn[r][ch]) = make_uint4(pkn[0], pkn[1], pkn[2], pkn[3]);
     }
-    lds_barrier();
 
-    // ---- K^n^T in lane order: piece (m, sp, lane) holds, for lane (g, li), the tokens
-    // 32sp + 4g .. and 32sp + 16 + 4g .. of channel pi(m, li) ------------------------------
-    for (int p = tid; p < MT * 2 * 64; p += NT) {
-        const int m = p >> 7, sp = (p >> 6) & 1, pl = p & 63, pg = pl >> 4, pli = pl & 15;
-        const int c = 32 * (m >> 1) + 8 * (pli >> 2) + 4 * (m & 1) + (pli & 3);
-        const int ta = 32 * sp + 4 * pg;
-        uint32_t wv[4];
+    // Row operands (registers): Kr = k e^{Gamma_i - rho_w}, Qr likewise.  Column operand (LDS):
+    // k e^{rho_{w+1} - Gamma_i}.  Block: K~ = k e^{Gamma_i}, Q~ = q e^{Gamma_i} (lane order,
+    // straight from registers); K^n staged for transposition.
+    __device__ __forceinline__ void phase4(Smem& sm, char* blk) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int s = 0; s < KS; ++s) {
+            const int ch = 32 * s + 8 * g;
+            // two halves of the lane's eight channels (fewer values live at once)
+            uint32_t pkr[4], pqr[4], pkc[4], pkt[4], pqt[4], pkn[4];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int t = ta + 16 * hh + 2 * e;
-                wv[2 * hh + e] = static_cast<uint32_t>(sm.a.kn[t][c]) | (static_cast<uint32_t>(sm.a.kn[t + 1][c]) << 16);
+            for (int hh = 0; hh < 2; ++hh) {
+                // e^{rho_{w+1} - rho_w}, e^{rho_w} and e^{Gamma_n - rho_{w+1}} of the four channels
+                const float4 tw4 = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4 * hh]);
+                const float4 eR4 = *reinterpret_cast<const float4*>(&sm.pre[w][ch + 4 * hh]);
+                const float4 eN4 = *reinterpret_cast<const float4*>(&sm.suf[w][ch + 4 * hh]);
+                const float tws[4] = {tw4.x, tw4.y, tw4.z, tw4.w};
+                const float eRs[4] = {eR4.x, eR4.y, eR4.z, eR4.w};
+                const float eNs[4] = {eN4.x, eN4.y, eN4.z, eN4.w};
+                float vkr[4], vqr[4], vkc[4], vkt[4], vqt[4], vkn[4];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int e = 4 * hh + e4;
+                    const float tw = tws[e4], eR = eRs[e4], eN = eNs[e4];
+                    const float kf = P::at(pk[s], e), qf = P::at(pq[s], e);
+                    const float f = F[s][e];
+                    const float E = tw * fast_rcp(f);  // e^{rho_{w+1} - Gamma_i}
+                    vkr[e4] = kf * f;
+                    vqr[e4] = qf * f;
+                    vkc[e4] = kf * E;
+                    vkt[e4] = vkr[e4] * eR;
+                    vqt[e4] = vqr[e4] * eR;
+                    vkn[e4] = vkc[e4] * eN;
+                }
+#pragma unroll
+                for (int p2 = 0; p2 < 2; ++p2) {
+                    pkr[2 * hh + p2] = pack_bf16x2(vkr[2 * p2], vkr[2 * p2 + 1]);
+                    pqr[2 * hh + p2] = pack_bf16x2(vqr[2 * p2], vqr[2 * p2 + 1]);
+                    pkc[2 * hh + p2] = pack_bf16x2(vkc[2 * p2], vkc[2 * p2 + 1]);
+                    pkt[2 * hh + p2] = pack_bf16x2(vkt[2 * p2], vkt[2 * p2 + 1]);
+                    pqt[2 * hh + p2] = pack_bf16x2(vqt[2 * p2], vqt[2 * p2 + 1]);
+                    pkn[2 * hh + p2] = pack_bf16x2(vkn[2 * p2], vkn[2 * p2 + 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        *reinterpret_cast<uint4*>(blk + B::KN + p * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            kr[s] = make_uint4(pkr[0], pkr[1], pkr[2], pkr[3]);
+            qr[s] = make_uint4(pqr[0], pqr[1], pqr[2], pqr[3]);
+            const int piece = (w * KS + s) * 64 + lane;
+            sm.b.kc[piece] = make_uint4(pkc[0], pkc[1], pkc[2], pkc[3]);
+            *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) = make_uint4(pkt[0], pkt[1], pkt[2], pkt[3]);
+            *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) = make_uint4(pqt[0], pqt[1], pqt[2], pqt[3]);
+            *reinterpret_cast<uint4*>(&sm.a.kn[r][ch]) = make_uint4(pkn[0], pkn[1], pkn[2], pkn[3]);
+        }
     }
-    lds_barrier();  // the tile products below overwrite the K^n staging
 
-    // ---- lower 16x16 tiles (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
+    // K^n^T in lane order: piece (m, sp, lane) holds, for lane (g, li), the tokens
+    // 32sp + 4g .. and 32sp + 16 + 4g .. of channel pi(m, li)
+    __device__ __forceinline__ void phase5(Smem& sm, char* blk) {
+        for (int p = tid; p < MT * 2 * 64; p += 256) {
+            const int m = p >> 7, sp = (p >> 6) & 1, pl = p & 63, pg = pl >> 4, pli = pl & 15;
+            const int c = 32 * (m >> 1) + 8 * (pli >> 2) + 4 * (m & 1) + (pli & 3);
+            const int ta = 32 * sp + 4 * pg;
+            uint32_t wv[4];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int t = ta + 16 * hh + 2 * e;
+                    wv[2 * hh + e] = static_cast<uint32_t>(sm.a.kn[t][c]) | (static_cast<uint32_t>(sm.a.kn[t + 1][c]) << 16);
+                }
+            *reinterpret_cast<uint4*>(blk + B::KN + p * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+
+    // lower 16x16 tiles (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
     // carries e^{rho_{b+1} - Gamma_j}; it is rescaled per channel by e^{rho_w - rho_{b+1}}
     // (the reciprocal of tile w's own product on the diagonal, at most e^80).  Transposed
     // product: lane ends with four consecutive columns j of one row i.
-    {
-        const float bi = sm.beta[r];
+    __device__ __forceinline__ void phase6(Smem& sm, const float* beta) {
+        const float bi = beta[r];
         for (int b = 0; b <= w; ++b) {
             f32x4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
 #pragma unroll
@@ -469,10 +508,10 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
             }
         }
     }
-    lds_barrier();
 
-    // ---- diagonal blocks T_aa = (I + L_aa)^{-1}, fp32 forward substitution (wave 3) -------
-    if (w == 3) {
+    // diagonal blocks T_aa = (I + L_aa)^{-1}, fp32 forward substitution (wave 3)
+    __device__ __forceinline__ void phase7(Smem& sm, bf16_t (*Tb)[16][16]) {
+        if (w != 3) return;
         const int a = lane >> 4, j = lane & 15;
         float t[16];
 #pragma unroll
@@ -492,16 +531,16 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
         // column j of T_aa -> T block (row-major) and its transpose (row j)
         const int d = tri_index(a, a);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.b.out.T[d][i][j] = f32_to_bf16(t[i]);
+        for (int i = 0; i < 16; ++i) Tb[d][i][j] = f32_to_bf16(t[i]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             *reinterpret_cast<uint2*>(&sm.b.out.Tt[d][j][4 * q4]) =
                 make_uint2(pack_bf16x2(t[4 * q4], t[4 * q4 + 1]), pack_bf16x2(t[4 * q4 + 2], t[4 * q4 + 3]));
     }
-    lds_barrier();
 
-    // ---- off-diagonal blocks: T_ab = -T_aa sum_{m=b}^{a-1} L_am T_mb, column block b = wave
-    if (w < 3) {
+    // off-diagonal blocks: T_ab = -T_aa sum_{m=b}^{a-1} L_am T_mb, column block b = wave
+    __device__ __forceinline__ void phase8(Smem& sm, bf16_t (*Tb)[16][16]) {
+        if (w >= 3) return;
         const int b = w;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         for (int a = b + 1; a < 4; ++a) {
@@ -509,37 +548,102 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
             for (int m = b; m < a; ++m)
                 acc = mfma16(*reinterpret_cast<const uint2*>(&sm.a.t.L[tri_index(a, m)][li][4 * g]),
                              *reinterpret_cast<const uint2*>(&sm.b.out.Tt[tri_index(m, b)][li][4 * g]), acc);
-            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&sm.b.out.T[tri_index(a, a)][li][4 * g]),
+            const f32x4_t tab = mfma16(*reinterpret_cast<const uint2*>(&Tb[tri_index(a, a)][li][4 * g]),
                                        pack_bf16x4(acc), zero);
             // tab[rr] = -T_ab[4g + rr][li]
             const int d = tri_index(a, b);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.b.out.T[d][4 * g + rr][li] = f32_to_bf16(-tab[rr]);
+            for (int rr = 0; rr < 4; ++rr) Tb[d][4 * g + rr][li] = f32_to_bf16(-tab[rr]);
             *reinterpret_cast<uint2*>(&sm.b.out.Tt[d][li][4 * g]) =
                 make_uint2(pack_bf16x2(-tab[0], -tab[1]), pack_bf16x2(-tab[2], -tab[3]));
         }
     }
-    lds_barrier();
 
-    // ---- M = A_qk T (lower blocks): M_ab = sum_{m=b}^{a} A_qk[a][m] T_mb --------------------
+    // M = A_qk T (lower blocks): M_ab = sum_{m=b}^{a} A_qk[a][m] T_mb
+    __device__ __forceinline__ void phase9(Smem& sm, bf16_t (*Mb)[16][16]) {
 #pragma unroll
-    for (int slot2 = 0; slot2 < 3; ++slot2) {
-        const int job = w + slot2 * 4;
-        if (job < 10) {
-            const int a = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-            const int b = job - (a * (a + 1)) / 2;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            for (int m = b; m <= a; ++m)
-                acc = mfma16(*reinterpret_cast<const uint2*>(&sm.a.t.Aqk[tri_index(a, m)][li][4 * g]),
-                             *reinterpret_cast<const uint2*>(&sm.b.out.Tt[tri_index(m, b)][li][4 * g]), acc);
+        for (int slot2 = 0; slot2 < 3; ++slot2) {
+            const int job = w + slot2 * 4;
+            if (job < 10) {
+                const int a = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
+                const int b = job - (a * (a + 1)) / 2;
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b; m <= a; ++m)
+                    acc = mfma16(*reinterpret_cast<const uint2*>(&sm.a.t.Aqk[tri_index(a, m)][li][4 * g]),
+                                 *reinterpret_cast<const uint2*>(&sm.b.out.Tt[tri_index(m, b)][li][4 * g]), acc);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.b.out.M[job][4 * g + rr][li] = f32_to_bf16(acc[rr]);
+                for (int rr = 0; rr < 4; ++rr) Mb[job][4 * g + rr][li] = f32_to_bf16(acc[rr]);
+            }
         }
     }
+};
+
+// The chunk slot of a (chunk, head) workgroup -> (sequence, first token, valid tokens);
+// false for slots past the last chunk.
+__device__ __forceinline__ bool slot_chunk(const SplitArgs& args, int slot, int64_t& t0, int& clen) {
+    int n;
+    int64_t tok0, len, c0;
+    if (args.cu) {
+        if (slot >= args.chunk_start[args.n_seqs]) return false;
+        n = slot_seq(args.chunk_start, args.n_seqs, slot);
+        tok0 = args.cu[n];
+        len = static_cast<int64_t>(args.cu[n + 1]) - tok0;
+        c0 = static_cast<int64_t>(slot - args.chunk_start[n]) * kC;
+    } else {
+        const int nc = static_cast<int>((args.T + kC - 1) / kC);
+        n = slot / nc;
+        if (n >= args.n_seqs) return false;
+        tok0 = static_cast<int64_t>(n) * args.T;
+        len = args.T;
+        c0 = static_cast<int64_t>(slot - n * nc) * kC;
+    }
+    clen = static_cast<int>(len - c0 < kC ? len - c0 : kC);
+    t0 = tok0 + c0;
+    return true;
+}
+
+// One workgroup of four waves per (chunk, head); the factor block goes to global memory.
+template <int DK, typename TIn>
+__global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_kernel(SplitArgs args) {
+    using Smem = IntraSmem<DK>;
+    // four workgroups per CU (bf16 inputs, see the launch bounds) need their LDS to fit 160 KiB
+    static_assert(sizeof(Smem) * (sizeof(TIn) == 2 ? 4 : 2) <= 160 * 1024, "intra-chunk LDS budget");
+    using B = Block<DK>;
+    __shared__ Smem sm;
+
+    // workgroup -> (chunk slot, head), the head fastest: the workgroups in flight together
+    // read the same tokens' rows of every head, which lie next to each other in memory
+    const int H = args.H, slot = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
+    int64_t t0;
+    int clen;
+    if (!slot_chunk(args, slot, t0, clen)) return;
+    char* blk = static_cast<char*>(args.blocks) + (static_cast<size_t>(slot) * H + h) * B::BYTES;
+
+    Producer<DK, TIn> pr;
+    pr.init(threadIdx.x);
+    pr.load(args, h, t0, clen);
+    if (pr.tid < DK) sm.ae[pr.tid] = -expf(args.A[h * DK + pr.tid]) * kLog2e;
+    pr.phase1(sm.beta);
+    lds_barrier();
+    pr.phase2(sm, args.g_min * kLog2e);
+    lds_barrier();
+    pr.phase3(sm, blk);
+    lds_barrier();
+    pr.phase4(sm, blk);
+    lds_barrier();
+    pr.phase5(sm, blk);
+    lds_barrier();  // the tile products below overwrite the K^n staging
+    pr.phase6(sm, sm.beta);
+    lds_barrier();
+    pr.phase7(sm, sm.b.out.T);
+    lds_barrier();
+    pr.phase8(sm, sm.b.out.T);
+    lds_barrier();
+    pr.phase9(sm, sm.b.out.M);
     lds_barrier();
 
-    // ---- T and M lower blocks -> factor block (512 bytes per block, 16-byte pieces) -------
-    for (int idx = tid; idx < 2 * 10 * 32; idx += NT) {
+    // T and M lower blocks -> factor block (512 bytes per block, 16-byte pieces)
+    for (int idx = pr.tid; idx < 2 * 10 * 32; idx += 256) {
         const int which = idx / 320, rem = idx % 320;
         const uint4* src = which == 0 ? reinterpret_cast<const uint4*>(&sm.b.out.T[0][0][0])
                                       : reinterpret_cast<const uint4*>(&sm.b.out.M[0][0][0]);
@@ -1219,6 +1323,377 @@ __global__ void __launch_bounds__(64 * (2 + NLW)) prefill_state_lagged_kernel(Sp
     if (args.sN) store_state(args.sN + sbase);
 }
 
+// ---- fused prefill: intra-chunk factors and the state pass in one workgroup -------------
+// One workgroup of eight waves per (sequence, head) chain.  Waves 0-3 (producers) build
+// the factor block of chunk c + 1 into one LDS stage with the intra-chunk phases above, while
+// waves 4-7 (consumers) run the state pass over chunk c from the other stage, each owning
+// DK / 4 columns of the dk x dv state in MFMA accumulators.  The factor block never leaves
+// the CU, so the call moves only the method's own bytes through HBM: q, k, v, beta, z in, o
+// out, and the states.  The two groups share the workgroup barrier: every iteration runs the
+// producers' nine phase barriers, and the consumers place their three phases between them.
+// Producers load chunk c + 1's q, k, z and beta into the registers that chunk c's operands
+// have just released (after phase 4), so the loads are in flight during phases 5-9.
+template <int DK>
+struct FusedSmem {
+    struct Stage {
+        uint4 blk[Block<DK>::BYTES / 16];  // factor block in the state pass's LDS layout
+        float beta[kC];
+    };
+    IntraSmem<DK> p;  // producer scratch
+    Stage st[2];
+};
+
+// Consumer wave: NH halves of 16 state columns, [col0 + 16 h, col0 + 16 h + 16).  The state
+// rows are kept in the permuted order pi(m, i) of the state pass, so bf16-packing two
+// accumulator tiles gives each lane eight consecutive key channels.
+template <int DK, typename TIn>
+struct Consumer {
+    static constexpr int NH = DK / 64;
+    static constexpr int KS = DK / 32;
+    static constexpr int MT = DK / 16;
+    static constexpr int ES = static_cast<int>(sizeof(TIn));
+    using B = Block<DK>;
+    using Stage = typename FusedSmem<DK>::Stage;
+
+    int lane, g, li, col0;
+    f32x4_t S[NH][MT];
+    uint32_t vr[NH][4][4];  // v[16a + 4g + r][col0 + 16h + li] of the next chunk, as fp32 bits
+    uint2 Rb[NH][4];
+    uint2 Ub[NH][4];
+
+    // bf16-packed state, half h, K-step s: the eight key channels 32 s + 8 g .. of the lane
+    __device__ __forceinline__ uint4 packed_state(int h, int s) const {
+        return make_uint4(pack_bf16x2(S[h][2 * s][0], S[h][2 * s][1]),
+                          pack_bf16x2(S[h][2 * s][2], S[h][2 * s][3]),
+                          pack_bf16x2(S[h][2 * s + 1][0], S[h][2 * s + 1][1]),
+                          pack_bf16x2(S[h][2 * s + 1][2], S[h][2 * s + 1][3]));
+    }
+
+    // v rows of the chunk at token t0 with n_valid tokens (rows past the end read 0)
+    // (the lane's part of each offset is one VGPR; the row and half parts are wave-uniform and
+    // go in the instruction's scalar offset)
+    __device__ __forceinline__ void load_v(const char* vbase, uint32_t rowV, int64_t t0, int n_valid) {
+        const rsrc_t rv = make_rsrc(vbase + t0 * rowV, n_valid * rowV);
+        const uint32_t voff = static_cast<uint32_t>(4 * g) * rowV + static_cast<uint32_t>(col0 + li) * ES;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t soff = static_cast<uint32_t>(16 * a + r) * rowV + 16 * h * ES;
+                    if constexpr (sizeof(TIn) == 2)
+                        vr[h][a][r] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, voff, soff, 0)) << 16;
+                    else
+                        vr[h][a][r] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, soff, 0);
+                }
+    }
+
+    // X = K~ S, R = beta (V - X).  Rows past the chunk's end are zero without a test: v and
+    // beta read as zero there and K~ rows are zero.  The chunk's v was loaded after the
+    // previous chunk's last phase.
+    __device__ __forceinline__ void phaseA(const Stage& b) {
+        const uint4* kt = b.blk + B::KT / 16;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t X[NH][4];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) X[h][a] = zero;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 opd[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) opd[a] = kt[(a * KS + s) * 64 + lane];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const uint4 sb = packed_state(h, s);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) X[h][a] = mfma32(opd[a], sb, X[h][a]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // beta[16a + 4g + r], read once per row of 16 lanes and spread by DPP row broadcasts
+        const float bsrc = b.beta[16 * (li >> 2) + 4 * g + (li & 3)];
+        float4 bb[4];
+        bb[0] = make_float4(row_bcast<0>(bsrc), row_bcast<1>(bsrc), row_bcast<2>(bsrc), row_bcast<3>(bsrc));
+        bb[1] = make_float4(row_bcast<4>(bsrc), row_bcast<5>(bsrc), row_bcast<6>(bsrc), row_bcast<7>(bsrc));
+        bb[2] = make_float4(row_bcast<8>(bsrc), row_bcast<9>(bsrc), row_bcast<10>(bsrc), row_bcast<11>(bsrc));
+        bb[3] = make_float4(row_bcast<12>(bsrc), row_bcast<13>(bsrc), row_bcast<14>(bsrc), row_bcast<15>(bsrc));
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4_t R;
+                R[0] = bb[a].x * (__uint_as_float(vr[h][a][0]) - X[h][a][0]);
+                R[1] = bb[a].y * (__uint_as_float(vr[h][a][1]) - X[h][a][1]);
+                R[2] = bb[a].z * (__uint_as_float(vr[h][a][2]) - X[h][a][2]);
+                R[3] = bb[a].w * (__uint_as_float(vr[h][a][3]) - X[h][a][3]);
+                Rb[h][a] = pack_bf16x4(R);  // lane: R[16a + 4g + r][col li of half h]
+            }
+    }
+
+    // O^T = S^T Q~^T + R^T M^T (stored), U = T R
+    __device__ __forceinline__ void phaseB(const Stage& b, char* obase, uint32_t rowV, int64_t t0, int n_valid) {
+        const uint4* qt = b.blk + B::QT / 16;
+        const uint2* tb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
+        const uint2* mb = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t Yt[NH][4];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Yt[h][a] = zero;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 opd[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) opd[a] = qt[(a * KS + s) * 64 + lane];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const uint4 sb = packed_state(h, s);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) Yt[h][a] = mfma32(sb, opd[a], Yt[h][a]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // U = T R, chains over the source tile
+        {
+            uint2 tv[10];
+#pragma unroll
+            for (int t = 0; t < 10; ++t) tv[t] = tb[t * 64 + li * 4 + g];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                f32x4_t U[4] = {zero, zero, zero, zero};
+#pragma unroll
+                for (int bq = 0; bq < 4; ++bq)
+#pragma unroll
+                    for (int a = bq; a < 4; ++a) U[a] = mfma16(tv[tri_index(a, bq)], Rb[h][bq], U[a]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) Ub[h][a] = pack_bf16x4(U[a]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the M R chain starts from zero and Y^T is added on the VALU, so no accumulator
+        // passes from a 16x16x32 product to a 16x16x16 one
+        uint2 mv[10];
+#pragma unroll
+        for (int t = 0; t < 10; ++t) mv[t] = mb[t * 64 + li * 4 + g];
+        const rsrc_t ro = make_rsrc(obase + t0 * rowV, n_valid * rowV);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            f32x4_t Om[4] = {zero, zero, zero, zero};
+#pragma unroll
+            for (int bq = 0; bq < 4; ++bq)
+#pragma unroll
+                for (int a = bq; a < 4; ++a) Om[a] = mfma16(Rb[h][bq], mv[tri_index(a, bq)], Om[a]);
+            const uint32_t voff = static_cast<uint32_t>(li) * rowV + static_cast<uint32_t>(col0 + 4 * g) * ES;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                // Ot[r] = O[16a + li][col0 + 16h + 4g + r]
+                const f32x4_t Ot = Om[a] + Yt[h][a];
+                const uint32_t soff = static_cast<uint32_t>(16 * a) * rowV + 16 * h * ES;
+                if constexpr (sizeof(TIn) == 2) {
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2_t{pack_bf16x2(Ot[0], Ot[1]), pack_bf16x2(Ot[2], Ot[3])}, ro, voff, soff, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4_t{__float_as_uint(Ot[0]), __float_as_uint(Ot[1]), __float_as_uint(Ot[2]),
+                                __float_as_uint(Ot[3])}, ro, voff, soff, 0);
+                }
+            }
+        }
+    }
+
+    // S = diag(e^{Gamma_n}) S + K^n^T U
+    __device__ __forceinline__ void phaseC(const Stage& b) {
+        const uint4* kn = b.blk + B::KN / 16;
+        const float* dnv = reinterpret_cast<const float*>(b.blk + B::DN / 16);
+        // e^{Gamma_n} of state row 32 (j / 8) + 8 g + j % 8 for j = 4 m + r: lane li of a row
+        // reads j = 2 li, 2 li + 1 (wrapped inside the DK rows), DPP broadcasts spread them
+        const float2 dsrc = *reinterpret_cast<const float2*>(
+            &dnv[32 * ((li >> 2) & (DK / 32 - 1)) + 8 * g + 2 * (li & 3)]);
+        auto dj = [&](auto J) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            return row_bcast<j / 2>((j & 1) ? dsrc.y : dsrc.x);
+        };
+        auto scale = [&](auto M) __attribute__((always_inline)) {
+            constexpr int m = decltype(M)::value;
+            const float d0 = dj(std::integral_constant<int, 4 * m>{});
+            const float d1 = dj(std::integral_constant<int, 4 * m + 1>{});
+            const float d2 = dj(std::integral_constant<int, 4 * m + 2>{});
+            const float d3 = dj(std::integral_constant<int, 4 * m + 3>{});
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                S[h][m][0] *= d0;
+                S[h][m][1] *= d1;
+                S[h][m][2] *= d2;
+                S[h][m][3] *= d3;
+            }
+        };
+        scale(std::integral_constant<int, 0>{});
+        scale(std::integral_constant<int, 1>{});
+        scale(std::integral_constant<int, 2>{});
+        scale(std::integral_constant<int, 3>{});
+        if constexpr (MT > 4) {
+            scale(std::integral_constant<int, 4>{});
+            scale(std::integral_constant<int, 5>{});
+            scale(std::integral_constant<int, 6>{});
+            scale(std::integral_constant<int, 7>{});
+        }
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint4 kk = kn[(m * 2 + sp) * 64 + lane];
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    S[h][m] = mfma32(kk, make_uint4(Ub[h][2 * sp].x, Ub[h][2 * sp].y, Ub[h][2 * sp + 1].x,
+                                                    Ub[h][2 * sp + 1].y), S[h][m]);
+            }
+    }
+
+    // The state to / from one (sequence, head)'s dk x dv matrix at `base` (row stride dv = DK),
+    // this wave's columns.  Buffer accesses: one VGPR of lane offset, the row and half parts
+    // in the scalar offset, so no per-element 64-bit addresses stay live in the chunk loop.
+    __device__ __forceinline__ uint32_t state_voff() const {
+        return static_cast<uint32_t>(8 * g * DK + col0 + li) * 4;
+    }
+    __device__ __forceinline__ static uint32_t state_soff(int h, int m, int r) {
+        return static_cast<uint32_t>((32 * (m >> 1) + 4 * (m & 1) + r) * DK + 16 * h) * 4;
+    }
+    __device__ __forceinline__ void store_state(float* base) const {
+        const rsrc_t rs = make_rsrc(base, DK * DK * 4);
+        const uint32_t voff = state_voff();
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[h][m][r]), rs, voff,
+                                                          state_soff(h, m, r), 0);
+    }
+    __device__ __forceinline__ void load_state(const float* base) {
+        const rsrc_t rs = make_rsrc(base, base ? DK * DK * 4 : 0);  // no state: reads 0
+        const uint32_t voff = state_voff();
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[h][m][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, state_soff(h, m, r), 0));
+    }
+};
+
+template <int DK, typename TIn>
+__global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
+    using Sm = FusedSmem<DK>;
+    static_assert(sizeof(Sm) <= 160 * 1024, "fused prefill LDS budget");
+    constexpr int ES = static_cast<int>(sizeof(TIn));
+    __shared__ Sm sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // workgroup -> (chain rank, head), the head fastest; varlen chains run longest first
+    const int H = args.H;
+    if (static_cast<int>(blockIdx.x) >= args.npairs) return;
+    const int rank = static_cast<int>(blockIdx.x) / H, h = static_cast<int>(blockIdx.x) - rank * H;
+    const int n = args.cu ? args.chunk_start[rank] : rank;
+    const int64_t tok0 = seq_start(args.cu, args.T, n);
+    const int64_t len = (args.cu ? static_cast<int64_t>(args.cu[n + 1]) : tok0 + args.T) - tok0;
+    const int nchunks = static_cast<int>((len + kC - 1) / kC);
+    auto chunk_len = [&](int c) {
+        const int64_t rem = len - static_cast<int64_t>(c) * kC;
+        return rem < kC ? static_cast<int>(rem) : kC;
+    };
+
+    if (w < 4) {
+        // ================================ producers ================================
+        Producer<DK, TIn> pr;
+        pr.init(tid);
+        if (tid < DK) sm.p.ae[tid] = -expf(args.A[h * DK + tid]) * kLog2e;
+        const float gscale = args.g_min * kLog2e;
+        if (nchunks > 0) pr.load(args, h, tok0, chunk_len(0));
+        for (int c = 0; c <= nchunks; ++c) {
+            // iteration c builds chunk c's block in stage c % 2 (the consumers read the other)
+            const bool live = c < nchunks;
+            typename Sm::Stage& st = sm.st[c & 1];
+            char* blk = reinterpret_cast<char*>(st.blk);
+            bf16_t(*Tb)[16][16] = reinterpret_cast<bf16_t(*)[16][16]>(blk + Block<DK>::TB);
+            bf16_t(*Mb)[16][16] = reinterpret_cast<bf16_t(*)[16][16]>(blk + Block<DK>::MB);
+            if (live) pr.phase1(st.beta);
+            lds_barrier();
+            if (live) pr.phase2(sm.p, gscale);
+            lds_barrier();
+            if (live) pr.phase3(sm.p, blk);
+            lds_barrier();
+            if (live) pr.phase4(sm.p, blk);
+            // chunk c's q, k, z registers are free: load chunk c + 1 into them
+            if (c + 1 < nchunks) pr.load(args, h, tok0 + static_cast<int64_t>(c + 1) * kC, chunk_len(c + 1));
+            lds_barrier();
+            if (live) pr.phase5(sm.p, blk);
+            lds_barrier();
+            if (live) pr.phase6(sm.p, st.beta);
+            lds_barrier();
+            if (live) pr.phase7(sm.p, Tb);
+            lds_barrier();
+            if (live) pr.phase8(sm.p, Tb);
+            lds_barrier();
+            if (live) pr.phase9(sm.p, Mb);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ================================ consumers ================================
+    Consumer<DK, TIn> cs;
+    cs.lane = tid & 63;
+    cs.g = cs.lane >> 4;
+    cs.li = cs.lane & 15;
+    cs.col0 = (w - 4) * (DK / 4);
+    const int dv = DK;
+    const uint32_t rowV = static_cast<uint32_t>(H) * dv * ES;
+    const char* vbase = static_cast<const char*>(args.v) + (static_cast<size_t>(h) * dv) * ES;
+    char* obase = static_cast<char*>(args.o) + (static_cast<size_t>(h) * dv) * ES;
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * dv;
+    cs.load_state(args.s0 ? args.s0 + sbase : nullptr);
+    if (nchunks > 0) cs.load_v(vbase, rowV, tok0, chunk_len(0));
+    for (int c = 0; c <= nchunks; ++c) {
+        // iteration c runs the state pass over chunk c - 1 from stage (c - 1) % 2
+        const int e = c - 1;
+        const bool live = e >= 0;
+        const typename Sm::Stage& st = sm.st[e & 1];
+        const int64_t t0 = tok0 + static_cast<int64_t>(e) * kC;
+        // the consumer phases run beside the producers' longest phases: gates (2), operands
+        // (4) and tile products (6)
+        lds_barrier();
+        if (live) cs.phaseA(st);
+        lds_barrier();
+        lds_barrier();
+        if (live) cs.phaseB(st, obase, rowV, t0, chunk_len(e));
+        lds_barrier();
+        lds_barrier();
+        if (live) {
+            cs.phaseC(st);
+            if (c < nchunks) cs.load_v(vbase, rowV, tok0 + static_cast<int64_t>(c) * kC, chunk_len(c));
+            // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
+            if (args.ckpt && (e + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(e + 1) * kC <= len) {
+                const int j = (e + 1) / args.ckpt_chunks - 1;
+                const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
+                cs.store_state(args.ckpt + ((first + j) * H + h) * DK * dv);
+            }
+        }
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+    }
+    if (args.sN) cs.store_state(args.sN + sbase);
+}
+
 // ---- host side --------------------------------------------------------------------------
 
 size_t split_block_bytes(int dk) { return dk == 128 ? Block<128>::BYTES : Block<64>::BYTES; }
@@ -1258,8 +1733,24 @@ static hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// one fused workgroup of eight waves per (sequence, head); a varlen call first orders the
+// sequences (into the workspace's table, which the fused kernel reads as chain order)
+template <int DK, typename TIn>
+static hipError_t launch_fused_t(const SplitArgs& a, hipStream_t stream) {
+    if (a.cu) {
+        hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.n_seqs, a.chunk_start);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.npairs > 0)
+        hipLaunchKernelGGL((prefill_fused_kernel<DK, TIn>), dim3(static_cast<unsigned>(a.npairs)), dim3(512), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 template <int DK, typename TIn>
 static hipError_t launch_split_d(const SplitArgs& a, int ncw, hipStream_t stream) {
+    if (ncw == 0) return launch_fused_t<DK, TIn>(a, stream);
     // the lagged pass holds three Q~/M stages, which leave no LDS for fp32 v rows at d = 128
     if constexpr (DK == 64 || sizeof(TIn) == 2)
         if (ncw == 1) return launch_split_t<DK, 1, TIn, true>(a, stream);

@@ -13,8 +13,10 @@ The state pass runs one workgroup per (sequence, head, dv slice) with 1, 2 or 4 
 waves of 16 dv columns; the library halves the waves while the (sequence, head) pairs times
 slices still fit the compute units.  The rule, for dk = dv = d and P pairs on a device with
 U compute units: four waves if P * d / 32 > U, else two if P * d / 16 > U, else one.  With
-one wave, bf16 inputs (and every d = 64 call) take the lagged two-wave form.  Each case's
-pair count is derived from U so that it lands on the form it names.
+one wave, bf16 inputs (and every d = 64 call) take the lagged two-wave form.  With bf16
+inputs and P >= U, the fused single-kernel prefill runs instead (one workgroup per pair).
+Each case's pair count is derived from U so that it lands on the form it names (ncw = 0
+names the fused form).
 """
 from __future__ import annotations
 
@@ -33,7 +35,13 @@ def state_pass_waves(pairs: int, d: int, cus: int) -> int:
     return ncw
 
 
+def uses_fused(pairs: int, dtype: str, cus: int) -> bool:
+    return dtype == "bf16" and pairs >= cus
+
+
 def form_name(pairs: int, d: int, dtype: str, cus: int) -> str:
+    if uses_fused(pairs, dtype, cus):
+        return "fused"
     ncw = state_pass_waves(pairs, d, cus)
     if ncw == 1 and (dtype == "bf16" or d == 64):
         return "lagged"
@@ -41,7 +49,10 @@ def form_name(pairs: int, d: int, dtype: str, cus: int) -> str:
 
 
 def pairs_for(ncw: int, d: int, cus: int) -> int:
-    """A pair count that selects `ncw` compute waves: just inside each band."""
+    """A pair count that selects `ncw` compute waves (0: the fused form, bf16 only): just
+    inside each band."""
+    if ncw == 0:
+        return cus
     if ncw == 1:
         return cus * 16 // d
     if ncw == 2:
@@ -53,6 +64,8 @@ def case_shape(ncw: int, d: int, cus: int) -> Tuple[List[int], int]:
     """(lengths, H) with len(lengths) * H == pairs_for(ncw, d, cus)."""
     P = pairs_for(ncw, d, cus)
     H = 16 if P % 16 == 0 else 8 if P % 8 == 0 else 1
+    if ncw == 0:
+        H = 32 if P % 32 == 0 else H   # shorter chains for the oracle
     N = P // H
     return [LENGTHS[i % len(LENGTHS)] for i in range(N)], H
 

@@ -62,4 +62,7 @@ def test_carry_cases_land_on_every_form():
             P = len(lens) * H
             assert carry_cases.state_pass_waves(P, d, 256) == ncw, (d, ncw, P)
             assert carry_cases.form_name(P, d, "bf16", 256) == ("lagged" if ncw == 1 else f"waves{ncw}")
+        lens, H = carry_cases.case_shape(0, d, 256)
+        assert carry_cases.form_name(len(lens) * H, d, "bf16", 256) == "fused"
+        assert carry_cases.form_name(len(lens) * H, d, "fp32", 256) == "waves4"
     assert carry_cases.form_name(32, 128, "fp32", 256) == "waves1"
