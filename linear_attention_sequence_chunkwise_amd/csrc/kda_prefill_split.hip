@@ -459,7 +459,8 @@ struct Producer {
     // carries e^{rho_{b+1} - Gamma_j}; it is rescaled per channel by e^{rho_w - rho_{b+1}}
     // (the reciprocal of tile w's own product on the diagonal, at most e^80).  Transposed
     // product: lane ends with four consecutive columns j of one row i.
-    __device__ __forceinline__ void phase6(Smem& sm, const float* beta) {
+    __device__ __forceinline__ void phase6(Smem& sm, const float* beta, bf16_t (*Lb)[16][16],
+                                           bf16_t (*Ab)[16][16]) {
         const float bi = beta[r];
         for (int b = 0; b <= w; ++b) {
             f32x4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
@@ -498,12 +499,12 @@ struct Producer {
                     sm.a.t.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
                     qv[rr] = jj <= li ? cqk[rr] : 0.f;                // lower incl. diagonal
                 }
-                *reinterpret_cast<uint2*>(&sm.a.t.Aqk[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
             } else {
-                *reinterpret_cast<uint2*>(&sm.a.t.L[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&Lb[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(bi * ckk[0], bi * ckk[1]), pack_bf16x2(bi * ckk[2], bi * ckk[3]));
-                *reinterpret_cast<uint2*>(&sm.a.t.Aqk[job][li][4 * g]) =
+                *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
                     make_uint2(pack_bf16x2(cqk[0], cqk[1]), pack_bf16x2(cqk[2], cqk[3]));
             }
         }
@@ -633,7 +634,7 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
     lds_barrier();
     pr.phase5(sm, blk);
     lds_barrier();  // the tile products below overwrite the K^n staging
-    pr.phase6(sm, sm.beta);
+    pr.phase6(sm, sm.beta, sm.a.t.L, sm.a.t.Aqk);
     lds_barrier();
     pr.phase7(sm, sm.b.out.T);
     lds_barrier();
@@ -1325,12 +1326,16 @@ __global__ void __launch_bounds__(64 * (2 + NLW)) prefill_state_lagged_kernel(Sp
 
 // ---- fused prefill: intra-chunk factors and the state pass in one workgroup -------------
 // One workgroup of eight waves per (sequence, head) chain.  Waves 0-3 (producers) build
-// the factor block of chunk c + 1 into one LDS stage with the intra-chunk phases above, while
+// the factor block of chunk c + 1 into one LDS stage with intra-chunk phases 1-7 above, while
 // waves 4-7 (consumers) run the state pass over chunk c from the other stage, each owning
 // DK / 4 columns of the dk x dv state in MFMA accumulators.  The factor block never leaves
 // the CU, so the call moves only the method's own bytes through HBM: q, k, v, beta, z in, o
 // out, and the states.  The two groups share the workgroup barrier: every iteration runs the
-// producers' nine phase barriers, and the consumers place their three phases between them.
+// producers' seven phase barriers, and the consumers place their three phases between them.
+// Unlike the split path, the stage holds the diagonal blocks T_aa of T = (I + A_kk)^{-1}, the
+// strictly lower blocks L of A_kk and the blocks of A_qk: the consumers apply T by block
+// forward substitution, which takes the off-diagonal T blocks and M = A_qk T (phases 8-9)
+// off the producers' serial path.
 // Producers load chunk c + 1's q, k, z and beta into the registers that chunk c's operands
 // have just released (after phase 4), so the loads are in flight during phases 5-9.
 template <int DK>
@@ -1433,11 +1438,17 @@ struct Consumer {
             }
     }
 
-    // O^T = S^T Q~^T + R^T M^T (stored), U = T R
+    // U by block forward substitution over the four token tiles,
+    //   U_a = T_aa (R_a - sum_{m<a} L_am U_m),   L = the strictly lower A_kk blocks,
+    // which equals (I + A_kk)^{-1} R tile by tile; then the outputs
+    //   O_a = Q~_a S + sum_{m<=a} A_qk[a][m] U_m,
+    // formed transposed (O^T = S^T Q~^T + U^T A_qk^T) so each lane holds four adjacent output
+    // columns of one token, and stored.  Every 16x16x16 chain starts from zero and Y^T is added
+    // on the VALU, so no accumulator passes from a 16x16x32 product to a 16x16x16 one.
     __device__ __forceinline__ void phaseB(const Stage& b, char* obase, uint32_t rowV, int64_t t0, int n_valid) {
         const uint4* qt = b.blk + B::QT / 16;
-        const uint2* tb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
-        const uint2* mb = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
+        const uint2* lb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
+        const uint2* ab = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         f32x4_t Yt[NH][4];
 #pragma unroll
@@ -1457,37 +1468,35 @@ struct Consumer {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // U = T R, chains over the source tile
         {
-            uint2 tv[10];
+            uint2 lv[10];  // block (a, m), row li, columns 4g .. 4g + 3
 #pragma unroll
-            for (int t = 0; t < 10; ++t) tv[t] = tb[t * 64 + li * 4 + g];
+            for (int t = 0; t < 10; ++t) lv[t] = lb[t * 64 + li * 4 + g];
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                f32x4_t U[4] = {zero, zero, zero, zero};
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int bq = 0; bq < 4; ++bq)
+                for (int h = 0; h < NH; ++h) {
+                    f32x4_t acc = zero;
 #pragma unroll
-                    for (int a = bq; a < 4; ++a) U[a] = mfma16(tv[tri_index(a, bq)], Rb[h][bq], U[a]);
-#pragma unroll
-                for (int a = 0; a < 4; ++a) Ub[h][a] = pack_bf16x4(U[a]);
-            }
+                    for (int m = 0; m < a; ++m) acc = mfma16(lv[tri_index(a, m)], Ub[h][m], acc);
+                    const uint2 rb = Rb[h][a];
+                    const f32x4_t y = {lo_bf16(rb.x) - acc[0], hi_bf16(rb.x) - acc[1],
+                                       lo_bf16(rb.y) - acc[2], hi_bf16(rb.y) - acc[3]};
+                    Ub[h][a] = pack_bf16x4(mfma16(lv[tri_index(a, a)], pack_bf16x4(y), zero));
+                }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // the M R chain starts from zero and Y^T is added on the VALU, so no accumulator
-        // passes from a 16x16x32 product to a 16x16x16 one
-        uint2 mv[10];
+        uint2 av[10];
 #pragma unroll
-        for (int t = 0; t < 10; ++t) mv[t] = mb[t * 64 + li * 4 + g];
+        for (int t = 0; t < 10; ++t) av[t] = ab[t * 64 + li * 4 + g];
         const rsrc_t ro = make_rsrc(obase + t0 * rowV, n_valid * rowV);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             f32x4_t Om[4] = {zero, zero, zero, zero};
 #pragma unroll
-            for (int bq = 0; bq < 4; ++bq)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int a = bq; a < 4; ++a) Om[a] = mfma16(Rb[h][bq], mv[tri_index(a, bq)], Om[a]);
+                for (int a = m; a < 4; ++a) Om[a] = mfma16(Ub[h][m], av[tri_index(a, m)], Om[a]);
             const uint32_t voff = static_cast<uint32_t>(li) * rowV + static_cast<uint32_t>(col0 + 4 * g) * ES;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -1588,6 +1597,9 @@ struct Consumer {
     }
 };
 
+// The producer phases (1-based) beside which the consumers run their phases A, B and C
+constexpr int kSlotA = 2, kSlotB = 4, kSlotC = 6;
+
 template <int DK, typename TIn>
 __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
     using Sm = FusedSmem<DK>;
@@ -1622,8 +1634,9 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
             const bool live = c < nchunks;
             typename Sm::Stage& st = sm.st[c & 1];
             char* blk = reinterpret_cast<char*>(st.blk);
+            // the stage's 16x16 block areas: T_aa and L_am (a > m) in one, A_qk in the other
             bf16_t(*Tb)[16][16] = reinterpret_cast<bf16_t(*)[16][16]>(blk + Block<DK>::TB);
-            bf16_t(*Mb)[16][16] = reinterpret_cast<bf16_t(*)[16][16]>(blk + Block<DK>::MB);
+            bf16_t(*Ab)[16][16] = reinterpret_cast<bf16_t(*)[16][16]>(blk + Block<DK>::MB);
             if (live) pr.phase1(st.beta);
             lds_barrier();
             if (live) pr.phase2(sm.p, gscale);
@@ -1636,13 +1649,9 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
             lds_barrier();
             if (live) pr.phase5(sm.p, blk);
             lds_barrier();
-            if (live) pr.phase6(sm.p, st.beta);
+            if (live) pr.phase6(sm.p, st.beta, Tb, Ab);
             lds_barrier();
             if (live) pr.phase7(sm.p, Tb);
-            lds_barrier();
-            if (live) pr.phase8(sm.p, Tb);
-            lds_barrier();
-            if (live) pr.phase9(sm.p, Mb);
             lds_barrier();
         }
         return;
@@ -1667,29 +1676,24 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
         const bool live = e >= 0;
         const typename Sm::Stage& st = sm.st[e & 1];
         const int64_t t0 = tok0 + static_cast<int64_t>(e) * kC;
-        // the consumer phases run beside the producers' longest phases: gates (2), operands
-        // (4) and tile products (6)
-        lds_barrier();
-        if (live) cs.phaseA(st);
-        lds_barrier();
-        lds_barrier();
-        if (live) cs.phaseB(st, obase, rowV, t0, chunk_len(e));
-        lds_barrier();
-        lds_barrier();
-        if (live) {
-            cs.phaseC(st);
-            if (c < nchunks) cs.load_v(vbase, rowV, tok0 + static_cast<int64_t>(c) * kC, chunk_len(c));
-            // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
-            if (args.ckpt && (e + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(e + 1) * kC <= len) {
-                const int j = (e + 1) / args.ckpt_chunks - 1;
-                const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
-                cs.store_state(args.ckpt + ((first + j) * H + h) * DK * dv);
+        // one consumer phase beside producer phases kSlotA, kSlotB and kSlotC (1-based), seven
+        // barriers per iteration, as for the producers
+#pragma unroll
+        for (int k = 1; k <= 7; ++k) {
+            if (live && k == kSlotA) cs.phaseA(st);
+            if (live && k == kSlotB) cs.phaseB(st, obase, rowV, t0, chunk_len(e));
+            if (live && k == kSlotC) {
+                cs.phaseC(st);
+                if (c < nchunks) cs.load_v(vbase, rowV, tok0 + static_cast<int64_t>(c) * kC, chunk_len(c));
+                // prefix-cache checkpoint: the state after every ckpt_chunks full chunks
+                if (args.ckpt && (e + 1) % args.ckpt_chunks == 0 && static_cast<int64_t>(e + 1) * kC <= len) {
+                    const int j = (e + 1) / args.ckpt_chunks - 1;
+                    const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
+                    cs.store_state(args.ckpt + ((first + j) * H + h) * DK * dv);
+                }
             }
+            lds_barrier();
         }
-        lds_barrier();
-        lds_barrier();
-        lds_barrier();
-        lds_barrier();
     }
     if (args.sN) cs.store_state(args.sN + sbase);
 }
