@@ -53,12 +53,32 @@ def decode_bytes_per_pair(dk: int, dv: int, elem: int):
     return 2 * dk * dv * 4 + prefill_algorithmic(dk, dv, elem)[1]
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and blank space removed, so a stored counter
-    summary stays valid across comment edits and is dropped by any code change."""
+_COMMON_SOURCES = ("kda_device.h", "kda_launch.h")
+
+
+def summary_sources(name: str):
+    """Kernel source files a profile summary depends on (None: all of them).  A prefill
+    summary also depends on the C ABI file, which chooses the prefill's kernels."""
+    if name.startswith("prefill_"):
+        return ("kda_prefill_split.hip", "kda_api.cpp") + _COMMON_SOURCES
+    if name.startswith(("decode_", "spec_decode_")):
+        return ("kda_decode.hip",) + _COMMON_SOURCES
+    if name.startswith("gate_"):
+        return ("kda_gate.hip",) + _COMMON_SOURCES
+    if name.startswith("output_gate_"):
+        return ("kda_epilogue.hip",) + _COMMON_SOURCES
+    if name.startswith("short_conv_"):
+        return ("kda_prologue.hip",) + _COMMON_SOURCES
+    return None
+
+
+def kernel_source_hash(files=None) -> str:
+    """Hash of the kernel sources (all of them, or the named files) with comments and blank
+    space removed, so a stored counter summary stays valid across comment edits and is
+    dropped by any code change to the sources it depends on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_sequence_chunkwise_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(os.listdir(csrc)) if files is None else sorted(files):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -67,19 +87,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each
-    scaled by what the same counter reads for a device copy of known size), if a summary for
-    the current kernel sources exists under profiles/ (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+def _summary(workload: str, kind: str):
+    """Text of profiles/<workload>_<kind>.txt if it was taken for the current sources of the
+    kernels it covers, else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kind}.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
-    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or m_hash.group(1) != kernel_source_hash(summary_sources(workload)):
         return None
-    return float(m_bytes.group(1))
+    return txt
+
+
+def read_traffic(workload: str):
+    """HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the same counter reads for a device copy of known size), if a summary for
+    the current kernel sources exists under profiles/ (else None)."""
+    txt = _summary(workload, "traffic")
+    m_bytes = txt and re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    return float(m_bytes.group(1)) if m_bytes else None
 
 
 def read_mfma(workload: str):
@@ -88,18 +115,194 @@ def read_mfma(workload: str):
     (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, including masked tiles and per-slice recompute) and
     the fraction of SIMD cycles the MFMA units were busy over the call's kernels
     (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs)."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_mfma.txt")
-    if not os.path.exists(path):
+    txt = _summary(workload, "mfma")
+    if txt is None:
         return None
-    txt = open(path).read()
-    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", txt)
     m_fl = re.search(r"executed_bf16_flops_per_launch:\s*([0-9.eE+]+)", txt)
     m_busy = re.search(r"mfma_busy_frac_per_launch:\s*([0-9.eE+-]+)", txt)
-    if not m_hash or not m_fl or not m_busy or m_hash.group(1) != kernel_source_hash():
+    if not m_fl or not m_busy:
         return None
     return {"executed_bf16_flops_per_launch": float(m_fl.group(1)),
             "mfma_busy_frac": float(m_busy.group(1)),
             "source": f"profiles/{workload}_mfma.txt"}
+
+
+# --- rocprofv3 summaries under profiles/ ---------------------------------------------------
+# The raw rocprofv3 output stays out of the repository; these functions turn it into the short
+# text summaries that the readers above use.  The runs they expect, one directory each under
+# RAW (R = the repository root; cd /tmp && export TMPDIR=/tmp first):
+#   <prefill workload>_kt        rocprofv3 --kernel-trace --stats -d RAW/<dir> -o kt
+#                                --output-format csv -- python3 R/bench.py PREFILL_ARGS
+#                                --steps 20 --warmup 3
+#   <prefill workload>_<C>       rocprofv3 --pmc <C> --kernel-trace -d RAW/<dir> -o p
+#                                --output-format csv -- python3 R/bench.py PREFILL_ARGS
+#                                --steps 2 --warmup 1 --calibration-copy-mib 1024
+#                                for C = FETCH_SIZE, WRITE_SIZE
+#   <prefill workload>_mfma      the same with --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+#                                SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE (no calibration copy)
+#   others_kt, others_<C>        the same two kinds of runs over OTHER_ARGS (decode, speculative
+#                                decode, output epilogue, input prologue and gate), counters
+#                                with --decode-steps 4
+# where PREFILL_ARGS = --workload <w> --extra-workloads none --no-cpu-baseline --no-decode and
+# OTHER_ARGS = --workload prefill_b1_h16_t4096_d128_bf16 --extra-workloads none --no-cpu-baseline.
+
+MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"
+_PRE = "cd /tmp && export TMPDIR=/tmp && "
+_PREFILL_KERNELS = ("kda::chunk_table_kernel", "kda::chain_order_kernel", "prefill_intra_kernel",
+                    "prefill_state", "prefill_fused_kernel")
+# summary name -> (kernel-name filters, what one launch is, filters counted in one launch)
+_OTHER_SUMMARIES = {
+    "decode_n512_h32_d128_bf16_256steps": (("decode_kernel<",), "decode_kernel (one kda_decode_step)"),
+    "spec_decode_n512_h32_d128_bf16_k4": (("decode_multi_kernel",),
+                                          "one verify-and-commit round (kda_decode_verify + kda_decode_commit)"),
+    "output_gate_rows4194304_dv128_bf16": (("output_gate_kernel",), "output_gate_kernel (one kda_output_gate call)"),
+    "short_conv_b4_t32768_c4096_w4_bf16": (("short_conv_kernel", "conv_cache_kernel"),
+                                           "one kda_short_conv call (sum over its kernels)"),
+    "gate_b4_t32768_h32_d128_f32": (("kda::gate_kernel",), "gate_kernel (one kda_gate call)"),
+}
+
+
+def _profile_commands(tag: str, workload: str):
+    if workload == "others":
+        args = ("--workload prefill_b1_h16_t4096_d128_bf16 --extra-workloads none --no-cpu-baseline")
+        kt = f"{args} --steps 2 --warmup 1"
+        pmc = f"{args} --steps 2 --warmup 1 --decode-steps 4 --calibration-copy-mib 1024"
+        mf = None
+    else:
+        args = f"--workload {workload} --extra-workloads none --no-cpu-baseline --no-decode"
+        kt = f"{args} --steps 20 --warmup 3"
+        pmc = f"{args} --steps 2 --warmup 1 --calibration-copy-mib 1024"
+        mf = f"{args} --steps 2 --warmup 1"
+    d = "$R/gpurun_out/prof"
+    cmds = {
+        "kt": f"{_PRE}rocprofv3 --kernel-trace --stats -d {d}/{tag}_kt -o kt --output-format csv -- "
+              f"python3 $R/bench.py {kt}",
+        "FETCH_SIZE": f"{_PRE}rocprofv3 --pmc FETCH_SIZE --kernel-trace -d {d}/{tag}_FETCH_SIZE -o p "
+                      f"--output-format csv -- python3 $R/bench.py {pmc}",
+        "WRITE_SIZE": f"{_PRE}rocprofv3 --pmc WRITE_SIZE --kernel-trace -d {d}/{tag}_WRITE_SIZE -o p "
+                      f"--output-format csv -- python3 $R/bench.py {pmc}",
+    }
+    if mf:
+        cmds["mfma"] = (f"{_PRE}rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace -d {d}/{tag}_mfma -o p "
+                        f"--output-format csv -- python3 $R/bench.py {mf}")
+    return cmds
+
+
+def _counter_rows(path: str):
+    import csv
+    per = {}
+    rows = list(csv.DictReader(open(path)))
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return rows, per
+
+
+def _short_name(k: str) -> str:
+    return k.split("(")[0]
+
+
+def _write_kernel_trace(name, raw_dir, cmd, filters, hsh, out_dir):
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(raw_dir, "kt_kernel_stats.csv"))))
+    out = [f"# {name}: kernel trace summary (rocprofv3 --kernel-trace --stats)", "",
+           "Command (repository root = $R, run on one MI355X):", "", "    " + cmd, "",
+           f"kernel_source_hash: {hsh}", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        if any(f in r["Name"] for f in filters):
+            out.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                       f"{float(r['Percentage']):.1f} |")
+    open(os.path.join(out_dir, f"{name}_kernel_trace.txt"), "w").write("\n".join(out) + "\n")
+
+
+def _write_traffic(name, raw_dirs, cmds, filters, launch, hsh, out_dir):
+    out = [f"# {name}: HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+           "Commands (repository root = $R, one counter per run):", ""]
+    out += ["    " + c for c in cmds]
+    out += ["", "Each counter is scaled by what it reads for the 1 GiB device copy "
+                "(`--calibration-copy-mib 1024`)", "that the same command runs before the timed region.", ""]
+    total = 0.0
+    for c, d in zip(("FETCH_SIZE", "WRITE_SIZE"), raw_dirs):
+        rows, per = _counter_rows(os.path.join(d, "p_counter_collection.csv"))
+        cal = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                     if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == c
+                     and int(r["Grid_Size"]) == 131072)[0][1]
+        fac = (1 << 20) / cal
+        kind = "reads" if c == "FETCH_SIZE" else "writes"
+        out.append(f"{c}: the 1 GiB calibration copy {kind} {cal:.1f} KiB -> scale factor {fac:.4f}")
+        for k, cs in per.items():
+            if not any(x in k for x in filters):
+                continue
+            v = cs[c]
+            mean = sum(v) / len(v)
+            out.append(f"  {_short_name(k)}: {mean:.1f} KiB per dispatch (mean of {len(v)}) -> "
+                       f"{mean * 1024 * fac / 1e6:.2f} MB")
+            total += mean * 1024 * fac
+    out += ["", f"launch: {launch}", f"kernel_source_hash: {hsh}", f"traffic_bytes_per_launch: {total:.6e}"]
+    open(os.path.join(out_dir, f"{name}_traffic.txt"), "w").write("\n".join(out) + "\n")
+    return total
+
+
+def _write_mfma(name, raw_dir, cmd, filters, hsh, out_dir):
+    rows, per = _counter_rows(os.path.join(raw_dir, "p_counter_collection.csv"))
+    out = [f"# {name}: MFMA counters per launch (rocprofv3 --pmc {MFMA_COUNTERS})", "",
+           "Command (repository root = $R, run on one MI355X):", "", "    " + cmd, "",
+           "Executed bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (counts masked tile entries and",
+           "per-slice work as executed).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs)",
+           "/ (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); GRBM_GUI_ACTIVE is summed over the 8 XCDs.", "",
+           "| kernel | dispatches | MFMA flops per dispatch | MFMA busy cycles | GUI active cycles (per XCD) | MFMA busy |",
+           "|---|---|---|---|---|---|"]
+    fl_tot = busy_tot = gui_tot = 0.0
+    for k, cs in per.items():
+        if not any(x in k for x in filters):
+            continue
+        mean = lambda c: sum(cs[c]) / len(cs[c])
+        mops, busy, gui = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE") / 8
+        fl = mops * 512
+        out.append(f"| `{_short_name(k)}` | {len(cs['GRBM_GUI_ACTIVE'])} | {fl:.4e} | {busy:.4e} | {gui:.4e} | "
+                   f"{busy / (gui * 1024):.4f} |")
+        fl_tot += fl
+        busy_tot += busy
+        gui_tot += gui
+    out += ["", "launch: one kda_prefill_fwd call (sum over its kernels)", f"kernel_source_hash: {hsh}",
+            f"executed_bf16_flops_per_launch: {fl_tot:.6e}",
+            f"mfma_busy_frac_per_launch: {busy_tot / (gui_tot * 1024):.6f}"]
+    open(os.path.join(out_dir, f"{name}_mfma.txt"), "w").write("\n".join(out) + "\n")
+
+
+def summarize_profiles(raw: str, out_dir: str = None):
+    """Write profiles/*.txt from the rocprofv3 runs under `raw` (layout above); every run
+    present is summarised, runs that are missing are skipped."""
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    from linear_attention_sequence_chunkwise_amd import workloads
+    done = []
+    for w in (workloads.PREFILL_VARLEN, workloads.PREFILL_B4, workloads.PREFILL_B1):
+        hsh = kernel_source_hash(summary_sources(w))
+        cmds = _profile_commands(w, w)
+        d = lambda k: os.path.join(raw, f"{w}_{k}")
+        if os.path.isdir(d("kt")):
+            _write_kernel_trace(w, d("kt"), cmds["kt"], _PREFILL_KERNELS, hsh, out_dir)
+            done.append(f"{w}_kernel_trace")
+        if os.path.isdir(d("FETCH_SIZE")) and os.path.isdir(d("WRITE_SIZE")):
+            _write_traffic(w, [d("FETCH_SIZE"), d("WRITE_SIZE")], [cmds["FETCH_SIZE"], cmds["WRITE_SIZE"]],
+                           _PREFILL_KERNELS, "one kda_prefill_fwd call (sum over its kernels)", hsh, out_dir)
+            done.append(f"{w}_traffic")
+        if os.path.isdir(d("mfma")):
+            _write_mfma(w, d("mfma"), cmds["mfma"], _PREFILL_KERNELS, hsh, out_dir)
+            done.append(f"{w}_mfma")
+    cmds = _profile_commands("others", "others")
+    d = lambda k: os.path.join(raw, f"others_{k}")
+    for name, (filters, launch) in _OTHER_SUMMARIES.items():
+        hsh = kernel_source_hash(summary_sources(name))
+        if os.path.isdir(d("kt")):
+            _write_kernel_trace(name, d("kt"), cmds["kt"], filters, hsh, out_dir)
+            done.append(f"{name}_kernel_trace")
+        if os.path.isdir(d("FETCH_SIZE")) and os.path.isdir(d("WRITE_SIZE")):
+            _write_traffic(name, [d("FETCH_SIZE"), d("WRITE_SIZE")], [cmds["FETCH_SIZE"], cmds["WRITE_SIZE"]],
+                           filters, launch, hsh, out_dir)
+            done.append(f"{name}_traffic")
+    return done
 
 
 def cpu_threads() -> int:
@@ -273,7 +476,15 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the timed "
                          "region (a known-size reference for HBM traffic counters)")
+    ap.add_argument("--summarize-profiles", metavar="RAW_DIR", default=None,
+                    help="write profiles/*.txt from the rocprofv3 runs under RAW_DIR and exit "
+                         "(no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        for name in summarize_profiles(args.summarize_profiles):
+            print(name)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one MI355X only; --gpus above 1 is not supported "

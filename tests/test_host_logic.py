@@ -136,6 +136,13 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     f.write_text(f.read_text().replace("acc.x += gv.x;", "acc.x += gv.x * 1.0f;"))
     assert bench.kernel_source_hash() != h0
+    # a summary depends only on its own kernels' sources: the gate change above leaves the
+    # decode summaries' hash alone and changes the gate summaries' one
+    h_dec = bench.kernel_source_hash(bench.summary_sources("decode_n512_h32_d128_bf16_256steps"))
+    h_gate = bench.kernel_source_hash(bench.summary_sources("gate_b4_t32768_h32_d128_f32"))
+    f.write_text(f.read_text().replace("acc.x += gv.x * 1.0f;", "acc.x += gv.x * 2.0f;"))
+    assert bench.kernel_source_hash(bench.summary_sources("decode_n512_h32_d128_bf16_256steps")) == h_dec
+    assert bench.kernel_source_hash(bench.summary_sources("gate_b4_t32768_h32_d128_f32")) != h_gate
 
 
 def test_summary_readers_drop_stale_summaries(tmp_path, monkeypatch):
@@ -148,12 +155,50 @@ def test_summary_readers_drop_stale_summaries(tmp_path, monkeypatch):
     (prof / "old_traffic.txt").write_text("kernel_source_hash: 0000000000000000\n"
                                           "traffic_bytes_per_launch: 1e9\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda files=None: h)
     assert bench.read_traffic("w") == 1.5e9
     m = bench.read_mfma("w")
     assert m["executed_bf16_flops_per_launch"] == 2e10 and m["mfma_busy_frac"] == 0.05
     assert bench.read_traffic("old") is None
     assert bench.read_traffic("missing") is None and bench.read_mfma("missing") is None
+
+
+def test_summarize_profiles_from_rocprof_csv(tmp_path, monkeypatch):
+    """bench.py --summarize-profiles turns rocprofv3 CSV output into the summaries the readers
+    use: kernel trace rows, counter means scaled by the calibration copy, the launch's total."""
+    raw = tmp_path / "raw"
+    w = "prefill_b1_h16_t4096_d128_bf16"
+    (raw / f"{w}_kt").mkdir(parents=True)
+    (raw / f"{w}_kt" / "kt_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void kda::prefill_intra_kernel<128, unsigned short>(kda::SplitArgs)",2,60000,30000,60,29000,31000,1\n'
+        '"void kda::prefill_state_lagged_kernel<128, 4, unsigned short>(kda::SplitArgs)",2,40000,20000,40,19000,21000,1\n'
+        '"__amd_rocclr_copyBuffer",1,10,10,0.01,10,10,0\n')
+    head = '"Dispatch_Id","Kernel_Name","Grid_Size","Counter_Name","Counter_Value"\n'
+    for c, cal, vals in (("FETCH_SIZE", 524288.0, (1000.0, 3000.0)), ("WRITE_SIZE", 1048576.0, (500.0, 700.0))):
+        d = raw / f"{w}_{c}"
+        d.mkdir()
+        rows = [f'1,"__amd_rocclr_copyBuffer",131072,"{c}",{cal}',
+                f'2,"void kda::prefill_intra_kernel<128, unsigned short>(kda::SplitArgs)",262144,"{c}",{vals[0]}',
+                f'3,"void kda::prefill_state_lagged_kernel<128, 4, unsigned short>(kda::SplitArgs)",256,"{c}",{vals[1]}']
+        (d / "p_counter_collection.csv").write_text(head + "\n".join(rows) + "\n")
+    out = tmp_path / "profiles"
+    out.mkdir()
+    done = bench.summarize_profiles(str(raw), str(out))
+    assert sorted(done) == [f"{w}_kernel_trace", f"{w}_traffic"]
+    kt = (out / f"{w}_kernel_trace.txt").read_text()
+    assert "| `void kda::prefill_intra_kernel<128, unsigned short>` | 2 | 30.00 |" in kt
+    assert "__amd_rocclr_copyBuffer" not in kt and "rocprofv3 --kernel-trace --stats" in kt
+    tr = (out / f"{w}_traffic.txt").read_text()
+    # FETCH_SIZE reads half the copied bytes: scale 2; WRITE_SIZE all of them: scale 1
+    want = (1000 + 3000) * 1024 * 2 + (500 + 700) * 1024 * 1
+    got = float(re.search(r"traffic_bytes_per_launch:\s*([0-9.e+]+)", tr).group(1))
+    assert abs(got - want) / want < 1e-4
+    h = bench.kernel_source_hash(bench.summary_sources(w))
+    assert f"kernel_source_hash: {h}" in tr
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda files=None: h)
+    assert bench.read_traffic(w) == got
 
 
 def test_bench_refuses_more_than_one_gpu():
