@@ -235,6 +235,28 @@ __device__ __forceinline__ float row_shr_or_zero(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, true));
 }
 
+// x[(lane + 8) mod 16] within the lane's row of 16
+__device__ __forceinline__ uint32_t row_ror8(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x128, 0xf, 0xf, false));
+}
+
+// Half-row loads.  A row piece of 128 bytes that lanes 0-7 and 8-15 of a DPP row would each
+// need half of is fetched as one line per row: register a holds, in lanes 0-7, the first half
+// of rows 0-7 and, in lanes 8-15, the second half of rows 0-7; register b the same for rows
+// 8-15.  Afterwards lane i holds the first half of row i in a and the second half in b.
+__device__ __forceinline__ void unswap_halves(uint32_t& a, uint32_t& b, bool lo) {
+    const uint32_t ra = row_ror8(a), rb = row_ror8(b);
+    const uint32_t first = lo ? a : rb, second = lo ? ra : b;
+    a = first;
+    b = second;
+}
+__device__ __forceinline__ void unswap_halves(uint4& a, uint4& b, bool lo) {
+    unswap_halves(a.x, b.x, lo);
+    unswap_halves(a.y, b.y, lo);
+    unswap_halves(a.z, b.z, lo);
+    unswap_halves(a.w, b.w, lo);
+}
+
 __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
     const uint4& u = e < 4 ? a : b;
     const int i = e & 3;
@@ -256,14 +278,15 @@ __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
 //   phase 3  per-channel products of tile totals; e^{Gamma_n} -> block
 //   phase 4  operands: K~, Q~ -> block, column operand and K^n staging -> LDS
 //   phase 5  K^n^T -> block in lane order
-//   phase 6  the 10 lower 16x16 tiles of A_kk and A_qk
-//   phase 7  diagonal blocks of T (wave 3)
+//   phase 6  the 10 lower 16x16 tiles of A_kk and A_qk (fused kernel: with each wave's own
+//            diagonal block of T, phase6_solve)
+//   phase 7  diagonal blocks of T (wave 3; intra-chunk kernel)
 //   phase 8  off-diagonal blocks of T (waves 0-2)
 //   phase 9  M = A_qk T
 // The block (K~, Q~, K^n^T, e^{Gamma_n}) is written through `blk`: global memory for the
 // intra-chunk kernel, an LDS stage for the fused kernel.  T and M go to the LDS arrays Tb and
 // Mb (the fused kernel's stage, or staging that the intra-chunk kernel copies out).
-template <int DK, typename TIn>
+template <int DK, typename TIn, bool HalfRow = false>
 struct Producer {
     using Smem = IntraSmem<DK>;
     using P = Pair<TIn>;
@@ -289,7 +312,17 @@ struct Producer {
         r = 16 * w + li;
     }
 
-    // loads of the chunk of `n_valid` tokens starting at token t0 of head h
+    // loads of the chunk of `n_valid` tokens starting at token t0 of head h (rows past the end
+    // read 0).  With HalfRow (the fused kernel, whose loads are issued beside its other work)
+    // each 128-byte line of a row is fetched by one instruction (the half-row scheme of
+    // unswap_halves; the halves are put in place where phases 2 and 4 first use them):
+    //   z: the two 16-byte pieces of a lane's 32 bytes in K-step s go to pz[s][0] (rows 0-7 of
+    //      the tile) and pz[s][1] (rows 8-15);
+    //   bf16 q, k: K-steps 2p and 2p + 1 of a row go to pk[2p] (rows 0-7) and pk[2p + 1]
+    //      (rows 8-15).
+    // The intra-chunk kernel, which waits for its loads, fetches each lane's own row pieces.
+    static constexpr bool kHalfRowZ = HalfRow;
+    static constexpr bool kHalfRowKQ = HalfRow && sizeof(TIn) == 2;
     __device__ __forceinline__ void load(const SplitArgs& args, int h, int64_t t0, int n_valid) {
         clen = n_valid;
         const int H = args.H;
@@ -303,13 +336,24 @@ struct Producer {
         const rsrc_t rk = make_rsrc(kbase + t0 * rowK, clen * rowK);
         const rsrc_t rq = make_rsrc(qbase + t0 * rowK, clen * rowK);
         const rsrc_t rz = make_rsrc(zbase + t0 * rowZ, clen * rowZ);
+        const uint32_t lo_row = kHalfRowZ ? 16 * w + (li & 7) : r;
+        const uint32_t hi_row = kHalfRowZ ? lo_row + 8 : r;
+        const uint32_t zoff0 = kHalfRowZ ? (li < 8 ? 0u : 16u) : 0u, zoff1 = kHalfRowZ ? zoff0 : 16u;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
+            if constexpr (kHalfRowKQ) {
+                const uint32_t row = lo_row + 8 * (s & 1);
+                const uint32_t ch = 32 * ((s & ~1) + (li >> 3)) + 8 * g;
+                pk[s] = P::load8(rk, row * rowK + ch * ES);
+                pq[s] = P::load8(rq, row * rowK + ch * ES);
+            } else {
+                const uint32_t ch = 32 * s + 8 * g;
+                pk[s] = P::load8(rk, r * rowK + ch * ES);
+                pq[s] = P::load8(rq, r * rowK + ch * ES);
+            }
             const uint32_t ch = 32 * s + 8 * g;
-            pk[s] = P::load8(rk, r * rowK + ch * ES);
-            pq[s] = P::load8(rq, r * rowK + ch * ES);
-            pz[s][0] = bload16(rz, r * rowZ + ch * 4);
-            pz[s][1] = bload16(rz, r * rowZ + ch * 4 + 16);
+            pz[s][0] = bload16(rz, lo_row * rowZ + ch * 4 + zoff0);
+            pz[s][1] = bload16(rz, hi_row * rowZ + ch * 4 + zoff1);
         }
         if (tid < kC) {
             const rsrc_t rb = make_rsrc(bbase + t0 * rowB, clen * rowB);
@@ -328,6 +372,10 @@ struct Producer {
     // pages' 16-token bound, so the exponential is finite and normal in fp32.
     __device__ __forceinline__ void phase2(Smem& sm, float gscale) {
         const bool valid = r < clen;
+        if constexpr (kHalfRowZ) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) unswap_halves(pz[s][0], pz[s][1], li < 8);
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const float4 a0 = *reinterpret_cast<const float4*>(&sm.ae[32 * s + 8 * g]);
@@ -386,6 +434,13 @@ struct Producer {
     // k e^{rho_{w+1} - Gamma_i}.  Block: K~ = k e^{Gamma_i}, Q~ = q e^{Gamma_i} (lane order,
     // straight from registers); K^n staged for transposition.
     __device__ __forceinline__ void phase4(Smem& sm, char* blk) {
+        if constexpr (kHalfRowKQ) {
+#pragma unroll
+            for (int p = 0; p < KS / 2; ++p) {
+                unswap_halves(pk[2 * p].a, pk[2 * p + 1].a, li < 8);
+                unswap_halves(pq[2 * p].a, pq[2 * p + 1].a, li < 8);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int ch = 32 * s + 8 * g;
@@ -455,58 +510,117 @@ struct Producer {
         }
     }
 
-    // lower 16x16 tiles (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
+    // lower 16x16 tile (w, b), b <= w, of A_kk and A_qk.  The column operand of tile b
     // carries e^{rho_{b+1} - Gamma_j}; it is rescaled per channel by e^{rho_w - rho_{b+1}}
     // (the reciprocal of tile w's own product on the diagonal, at most e^80).  Transposed
     // product: lane ends with four consecutive columns j of one row i.
+    __device__ __forceinline__ void tile_products(Smem& sm, int b, f32x4_t& ckk, f32x4_t& cqk) {
+        ckk = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        cqk = ckk;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int ch = 32 * s + 8 * g;
+            uint4 col = sm.b.kc[(b * KS + s) * 64 + lane];
+            if (b != w - 1) {
+                float4 s0, s1;
+                if (b == w) {
+                    const float4 t0v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch]);
+                    const float4 t1v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4]);
+                    s0 = make_float4(fast_rcp(t0v.x), fast_rcp(t0v.y), fast_rcp(t0v.z), fast_rcp(t0v.w));
+                    s1 = make_float4(fast_rcp(t1v.x), fast_rcp(t1v.y), fast_rcp(t1v.z), fast_rcp(t1v.w));
+                } else {
+                    s0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch]);
+                    s1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch + 4]);
+                    if (b == w - 3) {
+                        const float4 u0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch]);
+                        const float4 u1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch + 4]);
+                        s0 = make_float4(s0.x * u0.x, s0.y * u0.y, s0.z * u0.z, s0.w * u0.w);
+                        s1 = make_float4(s1.x * u1.x, s1.y * u1.y, s1.z * u1.z, s1.w * u1.w);
+                    }
+                }
+                col = scale8(col, s0, s1);
+            }
+            ckk = mfma32(col, kr[s], ckk);
+            cqk = mfma32(col, qr[s], cqk);
+        }
+    }
+
+    // tile (w, b)'s results: the diagonal A_kk tile (strictly lower, times beta) to fp32
+    // scratch Ld for the solve, off-diagonal ones to Lb; A_qk (lower incl. the diagonal) to Ab
+    __device__ __forceinline__ void store_tile(Smem& sm, int b, float bi, const f32x4_t& ckk, const f32x4_t& cqk,
+                                               bf16_t (*Lb)[16][16], bf16_t (*Ab)[16][16]) {
+        const int job = tri_index(w, b);
+        if (b == w) {
+            float qv[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int jj = 4 * g + rr;
+                sm.a.t.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
+                qv[rr] = jj <= li ? cqk[rr] : 0.f;                // lower incl. diagonal
+            }
+            *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
+                make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
+        } else {
+            *reinterpret_cast<uint2*>(&Lb[job][li][4 * g]) =
+                make_uint2(pack_bf16x2(bi * ckk[0], bi * ckk[1]), pack_bf16x2(bi * ckk[2], bi * ckk[3]));
+            *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
+                make_uint2(pack_bf16x2(cqk[0], cqk[1]), pack_bf16x2(cqk[2], cqk[3]));
+        }
+    }
+
+    // the 10 lower tiles of A_kk and A_qk, row tile w in wave w
     __device__ __forceinline__ void phase6(Smem& sm, const float* beta, bf16_t (*Lb)[16][16],
                                            bf16_t (*Ab)[16][16]) {
         const float bi = beta[r];
         for (int b = 0; b <= w; ++b) {
-            f32x4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
+            f32x4_t ckk, cqk;
+            tile_products(sm, b, ckk, cqk);
+            store_tile(sm, b, bi, ckk, cqk, Lb, Ab);
+        }
+    }
+
+    // column j of T_aa = (I + L_aa)^{-1} by fp32 forward substitution from the strictly
+    // lower L_aa in Ld[a] (stored column by column)
+    __device__ __forceinline__ static void solve_column(const float (*Ld)[20], int j, float (&t)[16]) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int ch = 32 * s + 8 * g;
-                uint4 col = sm.b.kc[(b * KS + s) * 64 + lane];
-                if (b != w - 1) {
-                    float4 s0, s1;
-                    if (b == w) {
-                        const float4 t0v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch]);
-                        const float4 t1v = *reinterpret_cast<const float4*>(&sm.ttile[w][ch + 4]);
-                        s0 = make_float4(fast_rcp(t0v.x), fast_rcp(t0v.y), fast_rcp(t0v.z), fast_rcp(t0v.w));
-                        s1 = make_float4(fast_rcp(t1v.x), fast_rcp(t1v.y), fast_rcp(t1v.z), fast_rcp(t1v.w));
-                    } else {
-                        s0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch]);
-                        s1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 1][ch + 4]);
-                        if (b == w - 3) {
-                            const float4 u0 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch]);
-                            const float4 u1 = *reinterpret_cast<const float4*>(&sm.ttile[w - 2][ch + 4]);
-                            s0 = make_float4(s0.x * u0.x, s0.y * u0.y, s0.z * u0.z, s0.w * u0.w);
-                            s1 = make_float4(s1.x * u1.x, s1.y * u1.y, s1.z * u1.z, s1.w * u1.w);
-                        }
-                    }
-                    col = scale8(col, s0, s1);
-                }
-                ckk = mfma32(col, kr[s], ckk);
-                cqk = mfma32(col, qr[s], cqk);
-            }
-            const int job = tri_index(w, b);
-            if (b == w) {
-                float qv[4];
+        for (int i = 0; i < 16; ++i) t[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int jj = 4 * g + rr;
-                    sm.a.t.Ld[w][jj][li] = jj < li ? bi * ckk[rr] : 0.f;  // strictly lower
-                    qv[rr] = jj <= li ? cqk[rr] : 0.f;                // lower incl. diagonal
-                }
-                *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
-                    make_uint2(pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]));
-            } else {
-                *reinterpret_cast<uint2*>(&Lb[job][li][4 * g]) =
-                    make_uint2(pack_bf16x2(bi * ckk[0], bi * ckk[1]), pack_bf16x2(bi * ckk[2], bi * ckk[3]));
-                *reinterpret_cast<uint2*>(&Ab[job][li][4 * g]) =
-                    make_uint2(pack_bf16x2(cqk[0], cqk[1]), pack_bf16x2(cqk[2], cqk[3]));
+        for (int m = 0; m < 15; ++m) {
+            float Lm[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(&Ld[m][4 * q4]);
+                Lm[4 * q4] = v4.x; Lm[4 * q4 + 1] = v4.y; Lm[4 * q4 + 2] = v4.z; Lm[4 * q4 + 3] = v4.w;
             }
+            const float tm = t[m];
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) t[i] -= Lm[i] * tm;
+        }
+    }
+
+    // the fused path's phase 6: each wave forms its diagonal tile first and solves its own
+    // T_ww right away (the wave reads back only what it wrote, so no barrier), then its
+    // off-diagonal tiles, so no later phase waits on one wave solving all four blocks
+    __device__ __forceinline__ void phase6_solve(Smem& sm, const float* beta, bf16_t (*Lb)[16][16],
+                                                 bf16_t (*Ab)[16][16], bf16_t (*Tb)[16][16]) {
+        const float bi = beta[r];
+        {
+            f32x4_t ckk, cqk;
+            tile_products(sm, w, ckk, cqk);
+            store_tile(sm, w, bi, ckk, cqk, Lb, Ab);
+        }
+        // every lane solves column li (the four rows of 16 lanes redundantly); row 0 stores it
+        float t[16];
+        solve_column(sm.a.t.Ld[w], li, t);
+        if (g == 0) {
+            const int d = tri_index(w, w);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tb[d][i][li] = f32_to_bf16(t[i]);
+        }
+        for (int b = 0; b < w; ++b) {
+            f32x4_t ckk, cqk;
+            tile_products(sm, b, ckk, cqk);
+            store_tile(sm, b, bi, ckk, cqk, Lb, Ab);
         }
     }
 
@@ -515,20 +629,7 @@ struct Producer {
         if (w != 3) return;
         const int a = lane >> 4, j = lane & 15;
         float t[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) t[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < 15; ++m) {
-            float Lm[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(&sm.a.t.Ld[a][m][4 * q4]);
-                Lm[4 * q4] = v4.x; Lm[4 * q4 + 1] = v4.y; Lm[4 * q4 + 2] = v4.z; Lm[4 * q4 + 3] = v4.w;
-            }
-            const float tm = t[m];
-#pragma unroll
-            for (int i = m + 1; i < 16; ++i) t[i] -= Lm[i] * tm;
-        }
+        solve_column(sm.a.t.Ld[a], j, t);
         // column j of T_aa -> T block (row-major) and its transpose (row j)
         const int d = tri_index(a, a);
 #pragma unroll
@@ -1326,18 +1427,21 @@ __global__ void __launch_bounds__(64 * (2 + NLW)) prefill_state_lagged_kernel(Sp
 
 // ---- fused prefill: intra-chunk factors and the state pass in one workgroup -------------
 // One workgroup of eight waves per (sequence, head) chain.  Waves 0-3 (producers) build
-// the factor block of chunk c + 1 into one LDS stage with intra-chunk phases 1-7 above, while
+// the factor block of chunk c + 1 into one LDS stage with intra-chunk phases 1-6 above (phase
+// 6 in the form that also solves the diagonal blocks of T), while
 // waves 4-7 (consumers) run the state pass over chunk c from the other stage, each owning
 // DK / 4 columns of the dk x dv state in MFMA accumulators.  The factor block never leaves
 // the CU, so the call moves only the method's own bytes through HBM: q, k, v, beta, z in, o
 // out, and the states.  The two groups share the workgroup barrier: every iteration runs the
-// producers' seven phase barriers, and the consumers place their three phases between them.
+// producers' six phase barriers, and the consumers place their phases between them.
 // Unlike the split path, the stage holds the diagonal blocks T_aa of T = (I + A_kk)^{-1}, the
 // strictly lower blocks L of A_kk and the blocks of A_qk: the consumers apply T by block
 // forward substitution, which takes the off-diagonal T blocks and M = A_qk T (phases 8-9)
 // off the producers' serial path.
 // Producers load chunk c + 1's q, k, z and beta into the registers that chunk c's operands
-// have just released (after phase 4), so the loads are in flight during phases 5-9.
+// have released, at the start of phase 6: issued beside the LDS-heavy phases 4 and 5, the same
+// loads stalled those phases for thousands of cycles.  The consumers load the next chunk's v
+// after phase C, for the same reason.
 template <int DK>
 struct FusedSmem {
     struct Stage {
@@ -1365,6 +1469,7 @@ struct Consumer {
     uint32_t vr[NH][4][4];  // v[16a + 4g + r][col0 + 16h + li] of the next chunk, as fp32 bits
     uint2 Rb[NH][4];
     uint2 Ub[NH][4];
+    f32x4_t Yt[NH][4];      // Y^T = S^T Q~^T of the chunk, from phase Y to phase B
 
     // bf16-packed state, half h, K-step s: the eight key channels 32 s + 8 g .. of the lane
     __device__ __forceinline__ uint4 packed_state(int h, int s) const {
@@ -1445,12 +1550,10 @@ struct Consumer {
     // formed transposed (O^T = S^T Q~^T + U^T A_qk^T) so each lane holds four adjacent output
     // columns of one token, and stored.  Every 16x16x16 chain starts from zero and Y^T is added
     // on the VALU, so no accumulator passes from a 16x16x32 product to a 16x16x16 one.
-    __device__ __forceinline__ void phaseB(const Stage& b, char* obase, uint32_t rowV, int64_t t0, int n_valid) {
+    // Y^T = S^T Q~^T (S before this chunk's update)
+    __device__ __forceinline__ void phaseY(const Stage& b) {
         const uint4* qt = b.blk + B::QT / 16;
-        const uint2* lb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
-        const uint2* ab = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t Yt[NH][4];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -1468,6 +1571,12 @@ struct Consumer {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
+    __device__ __forceinline__ void phaseB(const Stage& b, char* obase, uint32_t rowV, int64_t t0, int n_valid) {
+        const uint2* lb = reinterpret_cast<const uint2*>(b.blk + B::TB / 16);
+        const uint2* ab = reinterpret_cast<const uint2*>(b.blk + B::MB / 16);
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
         {
             uint2 lv[10];  // block (a, m), row li, columns 4g .. 4g + 3
 #pragma unroll
@@ -1597,8 +1706,15 @@ struct Consumer {
     }
 };
 
-// The producer phases (1-based) beside which the consumers run their phases A, B and C
+// The fused path's producer phases per chunk (1-6, with the diagonal solve inside phase 6),
+// and those beside which the consumers run their phases A, B and C
+constexpr int kFusedPhases = 6;
 constexpr int kSlotA = 2, kSlotB = 4, kSlotC = 6;
+// The slot of phase Y (Y^T = S^T Q~^T): up to kSlotB it runs for the chunk in hand; from
+// kSlotC on it runs for the next chunk (after phase C has updated S; that chunk's Q~ is
+// complete after producer phase 4)
+constexpr int kSlotY = 6;
+static_assert(kSlotY <= kSlotB || (kSlotY >= kSlotC && kSlotY <= kFusedPhases), "phase Y slot");
 
 template <int DK, typename TIn>
 __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
@@ -1624,7 +1740,7 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
 
     if (w < 4) {
         // ================================ producers ================================
-        Producer<DK, TIn> pr;
+        Producer<DK, TIn, true> pr;
         pr.init(tid);
         if (tid < DK) sm.p.ae[tid] = -expf(args.A[h * DK + tid]) * kLog2e;
         const float gscale = args.g_min * kLog2e;
@@ -1644,14 +1760,12 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
             if (live) pr.phase3(sm.p, blk);
             lds_barrier();
             if (live) pr.phase4(sm.p, blk);
-            // chunk c's q, k, z registers are free: load chunk c + 1 into them
-            if (c + 1 < nchunks) pr.load(args, h, tok0 + static_cast<int64_t>(c + 1) * kC, chunk_len(c + 1));
             lds_barrier();
             if (live) pr.phase5(sm.p, blk);
             lds_barrier();
-            if (live) pr.phase6(sm.p, st.beta, Tb, Ab);
-            lds_barrier();
-            if (live) pr.phase7(sm.p, Tb);
+            // chunk c's q, k, z registers are free: load chunk c + 1 into them
+            if (c + 1 < nchunks) pr.load(args, h, tok0 + static_cast<int64_t>(c + 1) * kC, chunk_len(c + 1));
+            if (live) pr.phase6_solve(sm.p, st.beta, Tb, Ab, Tb);
             lds_barrier();
         }
         return;
@@ -1676,11 +1790,14 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
         const bool live = e >= 0;
         const typename Sm::Stage& st = sm.st[e & 1];
         const int64_t t0 = tok0 + static_cast<int64_t>(e) * kC;
-        // one consumer phase beside producer phases kSlotA, kSlotB and kSlotC (1-based), seven
-        // barriers per iteration, as for the producers
+        // one consumer phase beside producer phases kSlotA, kSlotB and kSlotC (1-based), as
+        // many barriers per iteration as the producers
 #pragma unroll
-        for (int k = 1; k <= 7; ++k) {
+        for (int k = 1; k <= kFusedPhases; ++k) {
             if (live && k == kSlotA) cs.phaseA(st);
+            if constexpr (kSlotY <= kSlotB) {
+                if (live && k == kSlotY) cs.phaseY(st);
+            }
             if (live && k == kSlotB) cs.phaseB(st, obase, rowV, t0, chunk_len(e));
             if (live && k == kSlotC) {
                 cs.phaseC(st);
@@ -1691,6 +1808,9 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
                     const int64_t first = args.ckpt_off ? args.ckpt_off[n] : static_cast<int64_t>(n) * args.ckpt_per_seq;
                     cs.store_state(args.ckpt + ((first + j) * H + h) * DK * dv);
                 }
+            }
+            if constexpr (kSlotY >= kSlotC) {
+                if (k == kSlotY && c < nchunks) cs.phaseY(sm.st[c & 1]);
             }
             lds_barrier();
         }
@@ -1754,7 +1874,12 @@ static hipError_t launch_fused_t(const SplitArgs& a, hipStream_t stream) {
 
 template <int DK, typename TIn>
 static hipError_t launch_split_d(const SplitArgs& a, int ncw, hipStream_t stream) {
-    if (ncw == 0) return launch_fused_t<DK, TIn>(a, stream);
+    // the fused kernel exists for bf16 inputs only (fp32 operands need more registers)
+    if constexpr (sizeof(TIn) == 2) {
+        if (ncw == 0) return launch_fused_t<DK, TIn>(a, stream);
+    } else {
+        if (ncw == 0) return hipErrorInvalidValue;
+    }
     // the lagged pass holds three Q~/M stages, which leave no LDS for fp32 v rows at d = 128
     if constexpr (DK == 64 || sizeof(TIn) == 2)
         if (ncw == 1) return launch_split_t<DK, 1, TIn, true>(a, stream);
