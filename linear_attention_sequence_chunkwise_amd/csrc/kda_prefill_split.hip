@@ -314,15 +314,12 @@ struct Producer {
 
     // loads of the chunk of `n_valid` tokens starting at token t0 of head h (rows past the end
     // read 0).  With HalfRow (the fused kernel, whose loads are issued beside its other work)
-    // each 128-byte line of a row is fetched by one instruction (the half-row scheme of
-    // unswap_halves; the halves are put in place where phases 2 and 4 first use them):
-    //   z: the two 16-byte pieces of a lane's 32 bytes in K-step s go to pz[s][0] (rows 0-7 of
-    //      the tile) and pz[s][1] (rows 8-15);
-    //   bf16 q, k: K-steps 2p and 2p + 1 of a row go to pk[2p] (rows 0-7) and pk[2p + 1]
-    //      (rows 8-15).
-    // The intra-chunk kernel, which waits for its loads, fetches each lane's own row pieces.
+    // each 128-byte line of a z row is fetched by one instruction (the half-row scheme of
+    // unswap_halves, undone where phase 2 first uses z): the two 16-byte pieces of a lane's 32
+    // bytes in K-step s go to pz[s][0] (rows 0-7 of the tile) and pz[s][1] (rows 8-15).  The
+    // same scheme for q and k (measured) cost more in phase 4 than it saved.  The intra-chunk
+    // kernel, which waits for its loads, fetches each lane's own row pieces.
     static constexpr bool kHalfRowZ = HalfRow;
-    static constexpr bool kHalfRowKQ = HalfRow && sizeof(TIn) == 2;
     __device__ __forceinline__ void load(const SplitArgs& args, int h, int64_t t0, int n_valid) {
         clen = n_valid;
         const int H = args.H;
@@ -341,17 +338,9 @@ struct Producer {
         const uint32_t zoff0 = kHalfRowZ ? (li < 8 ? 0u : 16u) : 0u, zoff1 = kHalfRowZ ? zoff0 : 16u;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if constexpr (kHalfRowKQ) {
-                const uint32_t row = lo_row + 8 * (s & 1);
-                const uint32_t ch = 32 * ((s & ~1) + (li >> 3)) + 8 * g;
-                pk[s] = P::load8(rk, row * rowK + ch * ES);
-                pq[s] = P::load8(rq, row * rowK + ch * ES);
-            } else {
-                const uint32_t ch = 32 * s + 8 * g;
-                pk[s] = P::load8(rk, r * rowK + ch * ES);
-                pq[s] = P::load8(rq, r * rowK + ch * ES);
-            }
             const uint32_t ch = 32 * s + 8 * g;
+            pk[s] = P::load8(rk, r * rowK + ch * ES);
+            pq[s] = P::load8(rq, r * rowK + ch * ES);
             pz[s][0] = bload16(rz, lo_row * rowZ + ch * 4 + zoff0);
             pz[s][1] = bload16(rz, hi_row * rowZ + ch * 4 + zoff1);
         }
@@ -434,13 +423,6 @@ struct Producer {
     // k e^{rho_{w+1} - Gamma_i}.  Block: K~ = k e^{Gamma_i}, Q~ = q e^{Gamma_i} (lane order,
     // straight from registers); K^n staged for transposition.
     __device__ __forceinline__ void phase4(Smem& sm, char* blk) {
-        if constexpr (kHalfRowKQ) {
-#pragma unroll
-            for (int p = 0; p < KS / 2; ++p) {
-                unswap_halves(pk[2 * p].a, pk[2 * p + 1].a, li < 8);
-                unswap_halves(pq[2 * p].a, pq[2 * p + 1].a, li < 8);
-            }
-        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int ch = 32 * s + 8 * g;
