@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from linear_attention_sequence_chunkwise_amd import kda, workloads
+from tests import carry_cases
 from tests.gpu_util import (OUT_TOL, STATE_TOL, gpu_prefill, max_abs, note, oracle_prefill,
                             state_rel_err)
 
@@ -68,9 +69,10 @@ def _many_short_lengths(n, seed):
 
 @pytest.mark.parametrize("dk,dtype", [(128, "bf16"), (64, "fp32")])
 def test_prefill_many_short_sequences(dk, dtype):
-    """1,500 short ragged sequences: the chunk table's scan runs over two 1,024-sequence blocks
-    with a carry, the intra-chunk grid searches 1,500 sequence starts, and the state pass runs
-    3,000 chains (pairs not a multiple of the 8 XCDs)."""
+    """1,500 short ragged sequences, 3,000 chains (not a multiple of the 8 XCDs).  bf16 runs the
+    fused kernel (the chain order sorts 1,500 sequences, most of them one chunk or empty);
+    fp32 runs the split path: the chunk table's scan over two 1,024-sequence blocks with a
+    carry, the intra-chunk grid's search of 1,500 sequence starts, and the state pass."""
     inp = workloads.prefill_inputs(_many_short_lengths(1500, 40 + dk), H=2, dk=dk, dv=dk,
                                    dtype=dtype, seed=41 + dk, s0_std=0.02,
                                    name=f"n1500_short_d{dk}_{dtype}")
@@ -96,10 +98,13 @@ def test_prefill_stress_gates(z_mean):
 
 
 def test_prefill_eight_wave_path():
-    """256 (sequence, head) chains: the state pass uses 64-column slices (four compute waves
-    and four loader waves per workgroup)."""
-    inp = workloads.prefill_inputs([80] * 16, H=16, dk=128, dv=128, dtype="bf16", seed=12,
-                                   s0_std=0.02, name="n16_h16_t80")
+    """128 (sequence, head) chains, fewer than the 256 compute units: the split path, whose
+    state pass uses 64-column slices (four compute waves and four loader waves per
+    workgroup)."""
+    inp = workloads.prefill_inputs([80] * 16, H=8, dk=128, dv=128, dtype="bf16", seed=12,
+                                   s0_std=0.02, name="n16_h8_t80")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert carry_cases.form_name(inp.N * inp.H, 128, "bf16", cus) == "waves4"
     _check_prefill(inp, use_cu=False)
 
 
