@@ -276,7 +276,8 @@ __device__ __forceinline__ float lane8(const uint4& a, const uint4& b, int e) {
 //   phase 1  beta -> LDS
 //   phase 2  gates, tile-local scans, F = e^{Gamma_i - rho_w}; tile totals -> LDS
 //   phase 3  per-channel products of tile totals; e^{Gamma_n} -> block
-//   phase 4  operands: K~, Q~ -> block, column operand and K^n staging -> LDS
+//   phase 4  operands: K~, Q~ -> block, column operand and K^n staging -> LDS (fused kernel:
+//            K^n^T straight into the block, and no phase 5)
 //   phase 5  K^n^T -> block in lane order
 //   phase 6  the 10 lower 16x16 tiles of A_kk and A_qk (fused kernel: with each wave's own
 //            diagonal block of T, phase6_solve)
@@ -421,8 +422,20 @@ struct Producer {
 
     // Row operands (registers): Kr = k e^{Gamma_i - rho_w}, Qr likewise.  Column operand (LDS):
     // k e^{rho_{w+1} - Gamma_i}.  Block: K~ = k e^{Gamma_i}, Q~ = q e^{Gamma_i} (lane order,
-    // straight from registers); K^n staged for transposition.
+    // straight from registers); K^n staged for transposition (phase 5), or with KnDirect (the
+    // fused kernel, whose block is in LDS) written element by element straight into the
+    // transposed lane order of phase 5, which then has nothing left to do.
+    template <bool KnDirect = false>
     __device__ __forceinline__ void phase4(Smem& sm, char* blk) {
+        // KnDirect: token 16w + li, channel 32s + 8g + e lands in piece
+        // (m, sp) = (2s + e / 4, w / 2), lane (li / 4, 4g + e % 4), 2-byte slot
+        // 2 (w % 2) + (li % 4) of the piece's eight tokens.  Tokens 2i and 2i + 1 of a channel
+        // share a 4-byte word, so lanes li and li ^ 1 swap halves (DPP) and each writes whole
+        // words: the even lane channel 2j of both tokens, the odd lane channel 2j + 1.
+        const int odd = li & 1;
+        char* const kn_lane = blk + B::KN + ((li >> 2) * 16 + 4 * g) * 16 + ((li & 3) >> 1) * 4 +
+                              (w >> 1) * 1024 + (w & 1) * 8 + odd * 16;
+        const uint32_t kn_sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int ch = 32 * s + 8 * g;
@@ -469,7 +482,19 @@ struct Producer {
             sm.b.kc[piece] = make_uint4(pkc[0], pkc[1], pkc[2], pkc[3]);
             *reinterpret_cast<uint4*>(blk + B::KT + piece * 16) = make_uint4(pkt[0], pkt[1], pkt[2], pkt[3]);
             *reinterpret_cast<uint4*>(blk + B::QT + piece * 16) = make_uint4(pqt[0], pqt[1], pqt[2], pqt[3]);
-            *reinterpret_cast<uint4*>(&sm.a.kn[r][ch]) = make_uint4(pkn[0], pkn[1], pkn[2], pkn[3]);
+            if constexpr (KnDirect) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // channel e = 2j + odd of tokens (li & ~1, li | 1)
+                    const uint32_t nb = static_cast<uint32_t>(
+                        __builtin_amdgcn_mov_dpp(static_cast<int>(pkn[j]), 0xb1, 0xf, 0xf, true));  // quad_perm [1,0,3,2]
+                    const int e = 2 * j;
+                    *reinterpret_cast<uint32_t*>(kn_lane + (2 * s + (e >> 2)) * 2048 + (e & 3) * 16) =
+                        __builtin_amdgcn_perm(nb, pkn[j], kn_sel);
+                }
+            } else {
+                *reinterpret_cast<uint4*>(&sm.a.kn[r][ch]) = make_uint4(pkn[0], pkn[1], pkn[2], pkn[3]);
+            }
         }
     }
 
@@ -1409,13 +1434,14 @@ __global__ void __launch_bounds__(64 * (2 + NLW)) prefill_state_lagged_kernel(Sp
 
 // ---- fused prefill: intra-chunk factors and the state pass in one workgroup -------------
 // One workgroup of eight waves per (sequence, head) chain.  Waves 0-3 (producers) build
-// the factor block of chunk c + 1 into one LDS stage with intra-chunk phases 1-6 above (phase
-// 6 in the form that also solves the diagonal blocks of T), while
+// the factor block of chunk c + 1 into one LDS stage with intra-chunk phases 1-4 and 6 above
+// (phase 4 writing K^n^T itself, phase 6 in the form that also solves the diagonal blocks of
+// T), while
 // waves 4-7 (consumers) run the state pass over chunk c from the other stage, each owning
 // DK / 4 columns of the dk x dv state in MFMA accumulators.  The factor block never leaves
 // the CU, so the call moves only the method's own bytes through HBM: q, k, v, beta, z in, o
 // out, and the states.  The two groups share the workgroup barrier: every iteration runs the
-// producers' six phase barriers, and the consumers place their phases between them.
+// producers' five phase barriers, and the consumers place their phases between them.
 // Unlike the split path, the stage holds the diagonal blocks T_aa of T = (I + A_kk)^{-1}, the
 // strictly lower blocks L of A_kk and the blocks of A_qk: the consumers apply T by block
 // forward substitution, which takes the off-diagonal T blocks and M = A_qk T (phases 8-9)
@@ -1688,14 +1714,15 @@ struct Consumer {
     }
 };
 
-// The fused path's producer phases per chunk (1-6, with the diagonal solve inside phase 6),
-// and those beside which the consumers run their phases A, B and C
-constexpr int kFusedPhases = 6;
-constexpr int kSlotA = 2, kSlotB = 4, kSlotC = 6;
+// The fused path's barrier slots per chunk: producer phases 1, 2, 3, 4 (which writes K^n^T
+// itself, so there is no phase 5) and 6 (with the diagonal solves); the consumers run A, B
+// and C beside phases 2, 4 and 6
+constexpr int kFusedPhases = 5;
+constexpr int kSlotA = 2, kSlotB = 4, kSlotC = 5;
 // The slot of phase Y (Y^T = S^T Q~^T): up to kSlotB it runs for the chunk in hand; from
 // kSlotC on it runs for the next chunk (after phase C has updated S; that chunk's Q~ is
 // complete after producer phase 4)
-constexpr int kSlotY = 6;
+constexpr int kSlotY = 5;
 static_assert(kSlotY <= kSlotB || (kSlotY >= kSlotC && kSlotY <= kFusedPhases), "phase Y slot");
 
 template <int DK, typename TIn>
@@ -1741,9 +1768,7 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
             lds_barrier();
             if (live) pr.phase3(sm.p, blk);
             lds_barrier();
-            if (live) pr.phase4(sm.p, blk);
-            lds_barrier();
-            if (live) pr.phase5(sm.p, blk);
+            if (live) pr.template phase4<true>(sm.p, blk);  // K^n^T straight into the stage
             lds_barrier();
             // chunk c's q, k, z registers are free: load chunk c + 1 into them
             if (c + 1 < nchunks) pr.load(args, h, tok0 + static_cast<int64_t>(c + 1) * kC, chunk_len(c + 1));
