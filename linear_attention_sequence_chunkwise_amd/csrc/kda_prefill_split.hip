@@ -316,7 +316,7 @@ struct Producer {
     // loads of the chunk of `n_valid` tokens starting at token t0 of head h (rows past the end
     // read 0).  With HalfRow (the fused kernel, whose loads are issued beside its other work)
     // each 128-byte line of a z row is fetched by one instruction (the half-row scheme of
-    // unswap_halves, undone where phase 2 first uses z): the two 16-byte pieces of a lane's 32
+    // unswap_halves, undone by unswap_z before phase 2): the two 16-byte pieces of a lane's 32
     // bytes in K-step s go to pz[s][0] (rows 0-7 of the tile) and pz[s][1] (rows 8-15).  The
     // same scheme for q and k (measured) cost more in phase 4 than it saved.  The intra-chunk
     // kernel, which waits for its loads, fetches each lane's own row pieces.
@@ -352,6 +352,15 @@ struct Producer {
         }
     }
 
+    // the half-row z loads in place (HalfRow; before phase 2 reads z).  The fused kernel does it
+    // at the end of phase 6, where the loads have landed and phase 2's VALU work is not near
+    __device__ __forceinline__ void unswap_z() {
+        if constexpr (kHalfRowZ) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) unswap_halves(pz[s][0], pz[s][1], li < 8);
+        }
+    }
+
     __device__ __forceinline__ void phase1(float* beta) {
         if (tid < kC) beta[tid] = __uint_as_float(sizeof(TIn) == 2 ? rbeta << 16 : rbeta);
     }
@@ -362,10 +371,6 @@ struct Producer {
     // pages' 16-token bound, so the exponential is finite and normal in fp32.
     __device__ __forceinline__ void phase2(Smem& sm, float gscale) {
         const bool valid = r < clen;
-        if constexpr (kHalfRowZ) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) unswap_halves(pz[s][0], pz[s][1], li < 8);
-        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const float4 a0 = *reinterpret_cast<const float4*>(&sm.ae[32 * s + 8 * g]);
@@ -1753,7 +1758,10 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
         pr.init(tid);
         if (tid < DK) sm.p.ae[tid] = -expf(args.A[h * DK + tid]) * kLog2e;
         const float gscale = args.g_min * kLog2e;
-        if (nchunks > 0) pr.load(args, h, tok0, chunk_len(0));
+        if (nchunks > 0) {
+            pr.load(args, h, tok0, chunk_len(0));
+            pr.unswap_z();
+        }
         for (int c = 0; c <= nchunks; ++c) {
             // iteration c builds chunk c's block in stage c % 2 (the consumers read the other)
             const bool live = c < nchunks;
@@ -1773,6 +1781,7 @@ __global__ void __launch_bounds__(512) prefill_fused_kernel(SplitArgs args) {
             // chunk c's q, k, z registers are free: load chunk c + 1 into them
             if (c + 1 < nchunks) pr.load(args, h, tok0 + static_cast<int64_t>(c + 1) * kC, chunk_len(c + 1));
             if (live) pr.phase6_solve(sm.p, st.beta, Tb, Ab, Tb);
+            if (c + 1 < nchunks) pr.unswap_z();
             lds_barrier();
         }
         return;
