@@ -108,6 +108,15 @@ def test_checkpoints_many_sequences():
     _check(inp, 64, use_cu=True)
 
 
+def test_checkpoints_fused_d64():
+    """300 sequences of 0-200 tokens at d = 64, one head (the fused kernel at d = 64)."""
+    lens = [int(x) for x in np.random.default_rng(36).integers(0, 201, 300)]
+    lens[:4] = [0, 64, 63, 128]
+    inp = workloads.prefill_inputs(lens, H=1, dk=64, dv=64, dtype="bf16", seed=36,
+                                   s0_std=0.02, name="ck_fused_d64")
+    _check(inp, 64, use_cu=True)
+
+
 def test_checkpoints_d64_fp32():
     inp = workloads.prefill_inputs([200, 256], H=3, dk=64, dv=64, dtype="fp32", seed=33,
                                    s0_std=0.02, name="ck_d64_fp32")

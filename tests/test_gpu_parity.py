@@ -143,6 +143,36 @@ def test_prefill_all_empty_sequences_copy_state():
     assert np.array_equal(S, inp.S0.numpy().astype(np.float64))
 
 
+def _fused_pairs_assert(inp):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if inp.N * inp.H < cus:
+        pytest.skip(f"{inp.N * inp.H} chains do not reach the fused form on {cus} CUs")
+    assert carry_cases.form_name(inp.N * inp.H, inp.dk, inp.dtype, cus) == "fused"
+
+
+def test_prefill_fused_all_empty_sequences_copy_state():
+    """300 empty sequences (one chain per compute unit or more: the fused kernel, where every
+    chain has zero chunks): no output rows, and the final state is the initial one bit for
+    bit."""
+    inp = workloads.prefill_inputs([0] * 300, H=1, dk=128, dv=128, dtype="bf16", seed=17,
+                                   s0_std=0.02, name="fused_all_empty")
+    _fused_pairs_assert(inp)
+    o, S = gpu_prefill(inp, use_cu=True)
+    assert o.shape[0] == 0
+    assert np.array_equal(S, inp.S0.numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_prefill_fused_one_long_many_short(dk):
+    """One 4,000-token sequence among 299 of 0-70 tokens (every edge length present), one head:
+    the fused kernel with its longest-first chain order, against the oracle on every pair."""
+    lens = [4000] + _many_short_lengths(299, 60 + dk)
+    inp = workloads.prefill_inputs(lens, H=1, dk=dk, dv=dk, dtype="bf16", seed=61 + dk,
+                                   s0_std=0.02, name=f"fused_long_short_d{dk}")
+    _fused_pairs_assert(inp)
+    _check_prefill(inp, use_cu=True)
+
+
 def test_split_resume_matches_single_call():
     """prefill(x[:m]) then prefill(x[m:], initial = that final state) == prefill(x), the
     prefix-cache restore path ("Kimi K3 Under the Hood", serving section)."""
