@@ -96,11 +96,17 @@ kda_status kda_gate(const float* z, const float* A, float* g, float* gcum,
 
 /*
  * kda_prefill_workspace_size -- bytes of device workspace kda_prefill_fwd needs for this
- * problem (a multiple of 256).  The prefill runs in two kernels: the first computes every
- * (chunk, head)'s intra-chunk factors in parallel into the workspace (58.5 KiB per chunk and
- * head at d = 128, 34 KiB at d = 64, for at most ceil(total/64) + n_seqs chunks); the
- * second runs the serial inter-chunk state pass over them.  The workspace also holds the
- * varlen chunk table.  Returns 0 for invalid sizes; the prefill call reports those.
+ * problem on the current device (a multiple of 256).  With bf16 inputs and at least one
+ * (sequence, head) chain per compute unit of the current device, the prefill is one fused
+ * kernel that keeps each chunk's factors on chip: the workspace then holds only a table of
+ * n_seqs + 1 int32 (the varlen chain order), 256 bytes per 64 sequences.  Otherwise the
+ * prefill runs in two kernels: the first computes every (chunk, head)'s intra-chunk factors
+ * in parallel into the workspace (58.5 KiB per chunk and head at d = 128, 34.25 KiB at d = 64,
+ * for at most ceil(total/64) + n_seqs chunks, after the same table); the second runs the
+ * serial inter-chunk state pass over them.  The form follows the device current at the
+ * call, so query with the device current that the prefill will run on (a size taken for a
+ * device with more compute units may be too small: KDA_ERR_WORKSPACE).  Returns 0 for
+ * invalid sizes; the prefill call reports those.
  */
 size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
                                   kda_dtype dt);
@@ -150,9 +156,11 @@ kda_status kda_prefill_fwd(kda_dtype dt, const void* q, const void* k, const voi
  *
  * All arguments of kda_prefill_fwd keep their meaning; there is no workspace argument.
  *   - The call is accepted only when kda_prefill_workspace_size(...) of the same sizes is at
- *     most KDA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 4096 tokens x 16 heads at d = 128, or
- *     about 1,100 (chunk, head) pairs); KDA_ERR_SCRATCH otherwise, checked on the host
- *     before anything else happens.
+ *     most KDA_NOALLOC_SCRATCH_BYTES (64 MiB).  In the two-kernel form that is about 1,100
+ *     (chunk, head) pairs at d = 128 (e.g. 4096 tokens x 16 heads); the fused form (bf16,
+ *     a chain per compute unit) needs only the chain-order table, so any bf16 batch with
+ *     that many chains fits.  KDA_ERR_SCRATCH otherwise, checked on the host before
+ *     anything else happens.
  *   - The array's device address is looked up once per device (hipGetSymbolAddress, on the
  *     first call with that device current); a failed lookup returns KDA_ERR_HIP.  The call
  *     itself allocates nothing (no hipMalloc, no library allocation).

@@ -43,6 +43,22 @@ int compute_units() {
     return cus;
 }
 
+// The prefill's form for np (sequence, head) chains on the current device: 0 for the fused
+// kernel, else the state pass's compute waves per workgroup (1, 2 or 4).
+int prefill_form(kda_dtype dt, int64_t np, int dk) {
+    const int cus = compute_units();
+    // With a chain for every compute unit, one fused workgroup per (sequence, head) keeps the
+    // factor blocks on chip (bf16 inputs; the fp32 form needs more registers than it has).
+    if (dt == KDA_BF16 && np >= cus) return 0;
+    // Each state-pass workgroup copies the whole factor block of every chunk, so narrow dv
+    // slices cost block re-reads (from L2: the slices of one head run on one XCD) but shorten
+    // the per-chunk critical path.  Halve the compute waves per workgroup (64 columns at
+    // most) while the chains still fit the compute units.
+    int ncw = 4;
+    while (ncw > 1 && np * (dk / (8 * ncw)) <= cus) ncw /= 2;
+    return ncw;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,9 +108,10 @@ kda_status kda_gate(const float* z, const float* A, float* g, float* gcum, int64
 
 size_t kda_prefill_workspace_size(int64_t total_tokens, int n_seqs, int H, int dk, int dv,
                                   kda_dtype dt) {
-    (void)dt;
     if (total_tokens < 0 || n_seqs <= 0 || H <= 0 || !supported_d(dk, dv)) return 0;
     if (total_tokens > kMaxElems / (static_cast<int64_t>(H) * dk)) return 0;
+    // the fused kernel keeps its factors in LDS and needs only the sequence-order table
+    if (prefill_form(dt, static_cast<int64_t>(n_seqs) * H, dk) == 0) return kda::fused_workspace_bytes(n_seqs);
     return kda::split_workspace_bytes(total_tokens, n_seqs, H, dk);
 }
 
@@ -169,21 +186,11 @@ kda_status prefill_impl(kda_dtype dt, const void* q, const void* k, const void* 
         a.ckpt_chunks = ck.interval / 64;
         a.ckpt_per_seq = cu_seqlens ? 0 : static_cast<int>(T_or_total / ck.interval);
     }
-    const size_t table = ((static_cast<size_t>(n_seqs) + 1) * 4 + 255) / 256 * 256;
+    // the form the workspace was sized for (kda_prefill_workspace_size); the fused form has
+    // no factor blocks in memory
+    const int ncw = prefill_form(dt, a.npairs, dk);
     a.chunk_start = static_cast<int32_t*>(workspace);
-    a.blocks = static_cast<char*>(workspace) + table;
-    // state pass: enough (sequence, head, dv slice) chains to cover the compute units
-    const int cus = compute_units();
-    // Each state-pass workgroup copies the whole factor block of every chunk, so narrow dv
-    // slices cost block re-reads (from L2: the slices of one head run on one XCD) but shorten
-    // the per-chunk critical path.  Halve the compute waves per workgroup (64 columns at
-    // most) while the chains still fit the compute units.
-    const int64_t np = a.npairs;
-    int ncw = 4;
-    while (ncw > 1 && np * (dk / (8 * ncw)) <= cus) ncw /= 2;
-    // With a chain for every compute unit, one fused workgroup per (sequence, head) keeps the
-    // factor blocks on chip (bf16 inputs; the fp32 form needs more registers than it has).
-    if (dt == KDA_BF16 && np >= cus) ncw = 0;
+    a.blocks = ncw == 0 ? nullptr : static_cast<char*>(workspace) + kda::fused_workspace_bytes(n_seqs);
     return kda::launch_prefill_split(a, dk, dt == KDA_BF16, ncw, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

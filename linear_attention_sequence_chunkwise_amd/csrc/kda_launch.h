@@ -55,6 +55,8 @@ struct SplitArgs : PrefillArgs {
 
 size_t split_block_bytes(int dk);
 int64_t split_max_chunks(int64_t total, int n_seqs);
+// Sequence-order table alone (what the fused form needs), and table plus factor blocks.
+size_t fused_workspace_bytes(int n_seqs);
 size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk);
 // State-pass workgroup shape: ncw (1, 2 or 4) compute waves of 16 dv columns each, or 0 for
 // the fused single-kernel prefill (one eight-wave workgroup per (sequence, head)).

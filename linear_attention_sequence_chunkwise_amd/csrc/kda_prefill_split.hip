@@ -1840,9 +1840,10 @@ size_t split_block_bytes(int dk) { return dk == 128 ? Block<128>::BYTES : Block<
 
 int64_t split_max_chunks(int64_t total, int n_seqs) { return (total + kC - 1) / kC + n_seqs; }
 
+size_t fused_workspace_bytes(int n_seqs) { return ((static_cast<size_t>(n_seqs) + 1) * 4 + 255) / 256 * 256; }
+
 size_t split_workspace_bytes(int64_t total, int n_seqs, int H, int dk) {
-    const size_t table = ((static_cast<size_t>(n_seqs) + 1) * 4 + 255) / 256 * 256;
-    return table + static_cast<size_t>(split_max_chunks(total, n_seqs)) * H * split_block_bytes(dk);
+    return fused_workspace_bytes(n_seqs) + static_cast<size_t>(split_max_chunks(total, n_seqs)) * H * split_block_bytes(dk);
 }
 
 // K1 then K2 (the lagged 16-column state pass, or NCW compute waves of 16 columns)

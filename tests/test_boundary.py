@@ -200,6 +200,27 @@ def test_workspace_size_is_aligned(lib):
         assert lib.kda_prefill_workspace_size(*args) % 256 == 0
 
 
+def test_workspace_size_follows_the_prefill_form(lib):
+    """Without a device the library sizes for 256 compute units (MI355X's count).  bf16 with a
+    (sequence, head) chain per compute unit takes the fused kernel, which keeps its factors on
+    chip and needs only the n_seqs + 1 int32 chain-order table (rounded up to 256 bytes);
+    fp32, or fewer chains, take the two-kernel form with one factor block per chunk and head
+    (58.5 KiB at d = 128, 34.25 KiB at d = 64) after that table."""
+    table = lambda n: ((n + 1) * 4 + 255) // 256 * 256
+    block = {128: 59904, 64: 35072}
+    split = lambda T, n, H, d: table(n) + (-(-T // 64) + n) * H * block[d]
+    assert block[128] == 58.5 * 1024 and block[64] == 34.25 * 1024
+    for T, n, H, d in [(293000, 64, 32, 128), (16384, 16, 16, 128), (4096, 256, 1, 64)]:
+        assert n * H >= 256
+        assert lib.kda_prefill_workspace_size(T, n, H, d, d, BF16) == table(n)
+        assert lib.kda_prefill_workspace_size(T, n, H, d, d, F32) == split(T, n, H, d)
+    # one chain short of the compute units: the two-kernel form
+    assert lib.kda_prefill_workspace_size(16320, 15, 17, 128, 128, BF16) == split(16320, 15, 17, 128)
+    # so a bf16 batch far beyond the scratch in the two-kernel form fits it when fused
+    assert lib.kda_prefill_workspace_size(293000, 64, 32, 128, 128, F32) > kda.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_prefill_workspace_size(293000, 64, 32, 128, 128, BF16) <= kda.NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():

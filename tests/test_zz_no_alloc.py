@@ -25,6 +25,8 @@ def _compare(inp):
     note(f"[noalloc] {inp.name}: {inp.total} tokens, H={inp.H}, d={inp.dk}, {inp.dtype}, "
          f"workspace {need} of {kda.NOALLOC_SCRATCH_BYTES} bytes")
     assert need <= kda.NOALLOC_SCRATCH_BYTES
+    if inp.dtype == "bf16" and inp.N * inp.H >= 256:
+        assert need == (inp.N + 1 + 63) // 64 * 256, "the fused form needs only the chain-order table"
     s_ref = torch.empty(shape, dtype=torch.float32, device="cuda")
     o_ref = kda.kda_prefill_fwd(q, k, v, beta, z, A, initial_state=s0, final_state=s_ref,
                                 cu_seqlens=cu, n_seqs=n)
@@ -38,7 +40,14 @@ def _compare(inp):
 
 
 def test_noalloc_equals_workspace_entry_on_calls_in_a_row():
+    # 16 sequences x 16 heads: a chain per compute unit of MI355X (256), so the fused kernel,
+    # whose scratch is the chain-order table alone (the two-kernel form would need about
+    # 250 MB here, beyond the scratch)
+    assert torch.cuda.get_device_properties(0).multi_processor_count <= 256
     calls = [
+        workloads.prefill_inputs([1500, 700, 1024, 64, 2100, 999, 1, 1200, 640, 1024, 333,
+                                  1777, 900, 1030, 2000, 1000], H=16, dk=128, dv=128,
+                                 dtype="bf16", seed=60, s0_std=0.2, name="noalloc_fused_varlen"),
         # the largest named single-GPU prefill that fits the scratch: one 4096-token sequence
         workloads.make(workloads.PREFILL_B1),
         # varlen with slow decay and initial states
