@@ -337,18 +337,37 @@ struct Producer {
         const uint32_t lo_row = kHalfRowZ ? 16 * w + (li & 7) : r;
         const uint32_t hi_row = kHalfRowZ ? lo_row + 8 : r;
         const uint32_t zoff0 = kHalfRowZ ? (li < 8 ? 0u : 16u) : 0u, zoff1 = kHalfRowZ ? zoff0 : 16u;
+        // The intra-chunk kernel waits for these loads in phase 2 (z) and phase 4 (k, q): z
+        // first lets k and q stay in flight through phases 2-3 (B=4 H=32 T=32768: 2.79 ->
+        // 2.76 ms).  The fused kernel waits for all of them at the end of phase 6, and there
+        // that order is slower (3.88 -> 3.97 ms on the varlen batch): k and q then land beside
+        // the gates' VALU work of phase 2.
+        constexpr bool kZFirst = !kHalfRowZ;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const uint32_t ch = 32 * s + 8 * g;
-            pk[s] = P::load8(rk, r * rowK + ch * ES);
-            pq[s] = P::load8(rq, r * rowK + ch * ES);
+            if constexpr (!kZFirst) {
+                pk[s] = P::load8(rk, r * rowK + ch * ES);
+                pq[s] = P::load8(rq, r * rowK + ch * ES);
+            }
             pz[s][0] = bload16(rz, lo_row * rowZ + ch * 4 + zoff0);
             pz[s][1] = bload16(rz, hi_row * rowZ + ch * 4 + zoff1);
         }
-        if (tid < kC) {
+        // (with z first, every thread loads: offsets of threads past the chunk lie beyond the
+        // buffer's range and read 0 without a memory access, and a load outside a branch keeps
+        // the compiler from waiting for it, and so for every load before it, on the spot)
+        if (kZFirst || tid < kC) {
             const rsrc_t rb = make_rsrc(bbase + t0 * rowB, clen * rowB);
             if constexpr (sizeof(TIn) == 2) rbeta = bload2(rb, tid * rowB);
             else rbeta = bload4(rb, tid * rowB);
+        }
+        if constexpr (kZFirst) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint32_t ch = 32 * s + 8 * g;
+                pk[s] = P::load8(rk, r * rowK + ch * ES);
+                pq[s] = P::load8(rq, r * rowK + ch * ES);
+            }
         }
     }
 
@@ -735,8 +754,12 @@ __global__ void __launch_bounds__(256, sizeof(TIn) == 2 ? 4 : 2) prefill_intra_k
 
     Producer<DK, TIn> pr;
     pr.init(threadIdx.x);
+    // the gate constants before the rows, by every thread (past DK they read 0), so the
+    // exponential after the row loads waits for them alone
+    const uint32_t a_bits = bload4(make_rsrc(args.A + h * DK, DK * 4), pr.tid * 4);
     pr.load(args, h, t0, clen);
-    if (pr.tid < DK) sm.ae[pr.tid] = -expf(args.A[h * DK + pr.tid]) * kLog2e;
+    __builtin_amdgcn_sched_barrier(0);
+    if (pr.tid < DK) sm.ae[pr.tid] = -expf(__uint_as_float(a_bits)) * kLog2e;
     pr.phase1(sm.beta);
     lds_barrier();
     pr.phase2(sm, args.g_min * kLog2e);
