@@ -6,6 +6,8 @@ There is no fallback: if libkda.so is missing or no GPU is present the calls rai
 from __future__ import annotations
 
 import ctypes
+import functools
+import itertools
 import os
 from typing import Optional
 
@@ -123,6 +125,19 @@ def _dev(*ts):
             raise ValueError(f"tensors on different devices ({dev} and {t.device})")
 
 
+def _on_tensor_device(fn):
+    """Run a binding call with its tensors' GPU current: the library launches on the current
+    HIP device and sizes the prefill workspace for it."""
+    @functools.wraps(fn)
+    def run(*args, **kwargs):
+        for a in itertools.chain(args, kwargs.values()):
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return run
+
+
 def _expect(name: str, t: Optional[torch.Tensor], shape, dtype: torch.dtype):
     """The kernels take plain pointers and trust these shapes: check them before any call."""
     if t is None:
@@ -133,6 +148,7 @@ def _expect(name: str, t: Optional[torch.Tensor], shape, dtype: torch.dtype):
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
 
 
+@_on_tensor_device
 def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
              gcum: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
              n_seqs: int = 1, chunk: int = 64, g_min: float = G_MIN, want_g: bool = True,
@@ -160,10 +176,13 @@ def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
 
 def kda_prefill_workspace_size(total_tokens: int, n_seqs: int, H: int, dk: int, dv: int,
                                dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes kda_prefill_fwd needs on the current device (the fused form, taken by
+    bf16 calls with a (sequence, head) chain per compute unit, needs only a small table)."""
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_prefill_workspace_size(total_tokens, n_seqs, H, dk, dv, code))
 
 
+@_on_tensor_device
 def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=None,
                     final_state=None, cu_seqlens=None, n_seqs: Optional[int] = None, o=None,
                     workspace=None, stream=None, checkpoints=None, checkpoint_offsets=None,
@@ -225,6 +244,7 @@ def kda_prefill_fwd(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=Non
     return o
 
 
+@_on_tensor_device
 def kda_prefill_fwd_noalloc(q, k, v, beta, z, A, g_min: float = G_MIN, initial_state=None,
                             final_state=None, cu_seqlens=None, n_seqs: Optional[int] = None,
                             o=None, stream=None):
@@ -262,6 +282,7 @@ def kda_prefill_fwd_noalloc(q, k, v, beta, z, A, g_min: float = G_MIN, initial_s
     return o
 
 
+@_on_tensor_device
 def kda_decode_step(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, stream=None):
     """One decode step; q,k,z [N,H,dk]; v [N,H,dv]; beta [N,H]; state [N,H,dk,dv] fp32 is
     updated in place.  Returns o [N,H,dv]."""
@@ -285,6 +306,7 @@ def kda_decode_step(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, st
     return o
 
 
+@_on_tensor_device
 def kda_decode_verify(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, stream=None):
     """Outputs of K draft tokens per sequence from the committed state (read only);
     q,k,z [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]; state [N,H,dk,dv] fp32.
@@ -309,6 +331,7 @@ def kda_decode_verify(q, k, v, beta, z, A, state, g_min: float = G_MIN, o=None, 
     return o
 
 
+@_on_tensor_device
 def kda_decode_commit(k, v, beta, z, A, state, accepted, g_min: float = G_MIN, stream=None):
     """Advance state [N,H,dk,dv] in place by the first accepted[n] (device int32 [N]) of the
     K draft tokens k,z [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]."""
@@ -329,6 +352,7 @@ def kda_decode_commit(k, v, beta, z, A, state, accepted, g_min: float = G_MIN, s
     return state
 
 
+@_on_tensor_device
 def kda_output_gate(o, gate, weight, eps: float = 1e-6, y=None, stream=None):
     """y = Sigmoid(gate) * o / sqrt(mean(o^2) + eps) * weight over the last axis (dv);
     o, gate [..., dv] of one dtype; weight [dv] fp32.  Returns y (new, or the given tensor)."""
@@ -347,6 +371,7 @@ def kda_output_gate(o, gate, weight, eps: float = 1e-6, y=None, stream=None):
     return y
 
 
+@_on_tensor_device
 def kda_short_conv(x, weight, cache_in=None, cache_out=None, cu_seqlens=None,
                    n_seqs: Optional[int] = None, l2_group: int = 0, y=None, stream=None):
     """y = Swish(ShortConv(x)) (then L2Norm over groups of l2_group channels); x [total, C];
