@@ -117,6 +117,17 @@ def test_checkpoints_fused_d64():
     _check(inp, 64, use_cu=True)
 
 
+def test_checkpoints_fused_batch_form():
+    """Eight equal sequences of 320 tokens at 32 heads: 256 chains, the fused kernel given
+    n_seqs and no cu_seqlens, so each sequence's checkpoints start at n * (320 // interval)."""
+    inp = workloads.prefill_inputs([320] * 8, H=32, dk=128, dv=128, dtype="bf16", seed=37,
+                                   s0_std=0.02, name="ck_fused_batch")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if inp.N * inp.H < cus:
+        pytest.skip(f"{inp.N * inp.H} chains do not reach the fused form on {cus} CUs")
+    _check(inp, 128, use_cu=False)
+
+
 def test_checkpoints_d64_fp32():
     inp = workloads.prefill_inputs([200, 256], H=3, dk=64, dv=64, dtype="fp32", seed=33,
                                    s0_std=0.02, name="ck_d64_fp32")

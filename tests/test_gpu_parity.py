@@ -173,6 +173,27 @@ def test_prefill_fused_one_long_many_short(dk):
     _check_prefill(inp, use_cu=True)
 
 
+@pytest.mark.parametrize("dk", [128, 64])
+def test_prefill_fused_equal_lengths_many_heads(dk):
+    """Six sequences of 200 tokens (a ragged last chunk) at 48 heads: 288 chains, so the fused
+    kernel, given n_seqs and no cu_seqlens (each workgroup's chain rank is its sequence), with
+    every workgroup index split by a division by H = 48."""
+    inp = workloads.prefill_inputs([200] * 6, H=48, dk=dk, dv=dk, dtype="bf16", seed=70 + dk,
+                                   s0_std=0.02, name=f"fused_eq_h48_d{dk}")
+    assert inp.equal_length
+    _fused_pairs_assert(inp)
+    _check_prefill(inp, use_cu=False)
+
+
+def test_prefill_fused_varlen_many_heads():
+    """The same head count over ragged lengths (empty, one token, one chunk, one chunk plus
+    one): the fused kernel with its chain order, 48 heads per sequence."""
+    inp = workloads.prefill_inputs([0, 1, 64, 65, 130, 200], H=48, dk=128, dv=128, dtype="bf16",
+                                   seed=72, s0_std=0.02, name="fused_varlen_h48")
+    _fused_pairs_assert(inp)
+    _check_prefill(inp, use_cu=True)
+
+
 def test_split_resume_matches_single_call():
     """prefill(x[:m]) then prefill(x[m:], initial = that final state) == prefill(x), the
     prefix-cache restore path ("Kimi K3 Under the Hood", serving section)."""
