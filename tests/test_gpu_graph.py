@@ -14,10 +14,12 @@ from tests.gpu_util import note
 pytestmark = pytest.mark.gpu
 
 
-def test_prefill_and_decode_graph_replays_match_eager():
-    inp = workloads.prefill_inputs([150, 0, 97, 64], H=4, dk=128, dv=128, dtype="bf16", seed=61,
-                                   s0_std=0.02, name="graph_varlen")
-    dec = workloads.decode_inputs(N=4, H=4, dk=128, dv=128, steps=3, dtype="bf16", seed=62,
+@pytest.mark.parametrize("H", [4, 64])
+def test_prefill_and_decode_graph_replays_match_eager(H):
+    """H = 4: 16 chains, the split kernels; H = 64: 256 chains, the fused kernel (on 256 CUs)."""
+    inp = workloads.prefill_inputs([150, 0, 97, 64], H=H, dk=128, dv=128, dtype="bf16", seed=61,
+                                   s0_std=0.02, name=f"graph_varlen_h{H}")
+    dec = workloads.decode_inputs(N=4, H=H, dk=128, dv=128, steps=3, dtype="bf16", seed=62,
                                   name="graph_decode")
     c = lambda t: t.cuda()
     q, k, v, b, z, A, s0 = map(c, (inp.q, inp.k, inp.v, inp.beta, inp.z, inp.A, inp.S0))

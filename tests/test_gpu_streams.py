@@ -1,8 +1,8 @@
 """Calls on several streams at once.  The library keeps no state between calls: everything a
 call uses lives in the caller's tensors and workspace, and it works on the stream it is given.
-So two prefills and a decode launched together on three streams (default priority), each
-with its own workspace, must give exactly the results of the same calls run one after
-another.
+So three prefills (two on the split kernels, one on the fused kernel) and a decode launched
+together on four streams (default priority), each with its own workspace, must give exactly
+the results of the same calls run one after another.
 """
 from __future__ import annotations
 
@@ -48,13 +48,17 @@ def test_concurrent_streams_match_sequential():
                                  s0_std=0.02, name="streams_b")
     d = workloads.decode_inputs(N=64, H=8, dk=128, dv=128, steps=2, dtype="bf16", seed=73,
                                 name="streams_decode")
+    # 256 chains: the fused kernel (on 256 CUs), beside the split calls above
+    f = workloads.prefill_inputs([300, 0, 77, 129], H=64, dk=128, dv=128, dtype="bf16", seed=74,
+                                 s0_std=0.02, name="streams_fused")
     run_a, out_a = _prefill_bufs(a, use_cu=True)
     run_b, out_b = _prefill_bufs(b, use_cu=False)
     run_d, out_d, reset_d = _decode_bufs(d)
-    outs = out_a + out_b + out_d
+    run_f, out_f = _prefill_bufs(f, use_cu=True)
+    outs = out_a + out_b + out_d + out_f
 
     main = torch.cuda.current_stream()
-    for run in (run_a, run_b, run_d):
+    for run in (run_a, run_b, run_d, run_f):
         run(main)
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs]
@@ -63,11 +67,12 @@ def test_concurrent_streams_match_sequential():
         t.zero_()
     reset_d()
     torch.cuda.synchronize()
-    streams = [torch.cuda.Stream() for _ in range(3)]
-    for s, run in zip(streams, (run_a, run_b, run_d)):
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s, run in zip(streams, (run_a, run_b, run_d, run_f)):
         s.wait_stream(main)
         run(s)
     torch.cuda.synchronize()
     same = [torch.equal(t, r) for t, r in zip(outs, ref)]
-    note(f"[streams] prefill varlen bf16 d128, prefill batch fp32 d64, decode 2 steps: identical = {same}")
+    note(f"[streams] prefill varlen bf16 d128, prefill batch fp32 d64, decode 2 steps, fused "
+         f"prefill: identical = {same}")
     assert all(same)
