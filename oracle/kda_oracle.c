@@ -167,7 +167,11 @@ static void recur_token(double *S, int dk, int dv, const double *alpha, const fl
 #endif
     for (j = 0; j < dv; ++j) vhat[j] = 0.0;
     for (c = 0; c < dk; ++c) {                          /* vhat = Sbar^T k */
+#if KDA_ORACLE_MUTANT == 12
+        double kc = (double)q[c];                       /* planted: predicted at q, not k */
+#else
         double kc = (double)k[c];
+#endif
         const double *row = S + (size_t)c * dv;
         for (j = 0; j < dv; ++j) vhat[j] += row[j] * kc;
     }
@@ -192,7 +196,11 @@ static void recur_token(double *S, int dk, int dv, const double *alpha, const fl
 #if KDA_ORACLE_MUTANT != 3
     for (j = 0; j < dv; ++j) o[j] = 0.0;
     for (c = 0; c < dk; ++c) {                          /* o = S_t^T q (read after write) */
+#if KDA_ORACLE_MUTANT == 10
+        double qc = (double)k[c];                       /* planted: read with k, not q */
+#else
         double qc = (double)q[c];
+#endif
         const double *row = S + (size_t)c * dv;
         for (j = 0; j < dv; ++j) o[j] += row[j] * qc;
     }
@@ -209,7 +217,11 @@ static void token_alpha(const double *g, const float *z, const float *A, double 
     for (int c = 0; c < dk; ++c) {
         double gc = g ? g[tok_off + c]
                       : gate_one((double)A[(size_t)h * dk + c], (double)z[tok_off + c], g_min);
+#if KDA_ORACLE_MUTANT == 11
+        alpha[c] = exp(-gc);                             /* planted: e^-g, growth, not decay */
+#else
         alpha[c] = exp(gc);                              /* alpha = e^g */
+#endif
     }
 }
 
