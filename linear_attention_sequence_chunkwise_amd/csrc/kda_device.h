@@ -90,9 +90,6 @@ __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, off, 0, 0);
 }
-__device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
-}
 
 // Streaming 16-byte global accesses for data that one kernel touches exactly once (inputs
 // read once, outputs written once): the nontemporal hint keeps them from displacing lines

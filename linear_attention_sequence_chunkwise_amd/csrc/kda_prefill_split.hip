@@ -1,4 +1,5 @@
-// kda_prefill_split.hip -- chunkwise KDA prefill for gfx950 in two kernels:
+// kda_prefill_split.hip -- chunkwise KDA prefill for gfx950, in one of two forms.
+// Split form (fewer (sequence, head) chains than compute units, or fp32 inputs), two kernels:
 //   K1 (intra): every (chunk, head) in parallel -- gate, decays, the 16-token tile products,
 //               T = (I + A_kk)^{-1} and M = A_qk T -- written as one compact factor block
 //   K2 (state): per (sequence, head, dv slice), the serial inter-chunk pass
@@ -6,6 +7,10 @@
 //               S <- diag(e^{Gamma_n}) S + K^n^T U
 // Only K2's short dependent chain is serial over chunks; everything that does not depend on
 // the state runs at full-GPU parallelism in K1.
+// Fused form (bf16, a chain per compute unit or more): prefill_fused_kernel, one eight-wave
+// workgroup per chain, whose producer waves build the next chunk's factors into LDS with
+// K1's phases while its consumer waves run K2's products on the current chunk, so the factor
+// blocks never leave the CU (described at the kernel, near the end of this file).
 //
 // Sources (page title, section):
 //   [K3 note] "Kimi K3: Architecture, Training, and Million-Token Agentic RL"
