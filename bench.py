@@ -173,7 +173,7 @@ def _profile_commands(tag: str, workload: str):
         kt = f"{args} --steps 20 --warmup 3"
         pmc = f"{args} --steps 2 --warmup 1 --calibration-copy-mib 1024"
         mf = f"{args} --steps 2 --warmup 1"
-    d = "$R/gpurun_out/prof"
+    d = "$RAW"  # the directory that collects rocprofv3's raw output
     cmds = {
         "kt": f"{_PRE}rocprofv3 --kernel-trace --stats -d {d}/{tag}_kt -o kt --output-format csv -- "
               f"python3 $R/bench.py {kt}",
@@ -205,7 +205,7 @@ def _write_kernel_trace(name, raw_dir, cmd, filters, hsh, out_dir):
     import csv
     rows = list(csv.DictReader(open(os.path.join(raw_dir, "kt_kernel_stats.csv"))))
     out = [f"# {name}: kernel trace summary (rocprofv3 --kernel-trace --stats)", "",
-           "Command (repository root = $R, run on one MI355X):", "", "    " + cmd, "",
+           "Command (repository root = $R, raw rocprofv3 output under $RAW, run on one MI355X):", "", "    " + cmd, "",
            f"kernel_source_hash: {hsh}", "",
            "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -218,7 +218,7 @@ def _write_kernel_trace(name, raw_dir, cmd, filters, hsh, out_dir):
 
 def _write_traffic(name, raw_dirs, cmds, filters, launch, hsh, out_dir):
     out = [f"# {name}: HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-           "Commands (repository root = $R, one counter per run):", ""]
+           "Commands (repository root = $R, raw rocprofv3 output under $RAW, one counter per run):", ""]
     out += ["    " + c for c in cmds]
     out += ["", "Each counter is scaled by what it reads for the 1 GiB device copy "
                 "(`--calibration-copy-mib 1024`)", "that the same command runs before the timed region.", ""]
@@ -247,7 +247,7 @@ def _write_traffic(name, raw_dirs, cmds, filters, launch, hsh, out_dir):
 def _write_mfma(name, raw_dir, cmd, filters, hsh, out_dir):
     rows, per = _counter_rows(os.path.join(raw_dir, "p_counter_collection.csv"))
     out = [f"# {name}: MFMA counters per launch (rocprofv3 --pmc {MFMA_COUNTERS})", "",
-           "Command (repository root = $R, run on one MI355X):", "", "    " + cmd, "",
+           "Command (repository root = $R, raw rocprofv3 output under $RAW, run on one MI355X):", "", "    " + cmd, "",
            "Executed bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (counts masked tile entries and",
            "per-slice work as executed).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs)",
            "/ (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); GRBM_GUI_ACTIVE is summed over the 8 XCDs.", "",
