@@ -86,6 +86,23 @@ def test_prefill_b4_h32_t32768_slow_decay_all_pairs():
     _check_all_pairs(inp, o, sN)
 
 
+def test_prefill_fused_long_chains_slow_decay_all_pairs():
+    """The fused kernel (8 sequences x 32 heads = 256 chains, one per compute unit) over chains
+    of 63 chunks with slow-decay gates z ~ N(-4, 1) and an initial state of unit scale, so the
+    state carried in the consumers' accumulators persists, and is rounded to bf16 for the
+    chunk products, over every chunk of every chain."""
+    inp = workloads.prefill_inputs([4000] * 8, H=32, dk=128, dv=128, dtype="bf16", seed=23,
+                                   z_mean=-4.0, s0_std=1.0,
+                                   name="prefill_b8_h32_t4000_d128_bf16_z-4_s0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if inp.N * inp.H < cus:
+        pytest.skip(f"{inp.N * inp.H} chains do not reach the fused form on {cus} CUs")
+    note(f"[full] {inp.name}")
+    o, sN = _run_full(inp, want_state=True)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(sN).all()
+    _check_all_pairs(inp, o, sN)
+
+
 def test_prefill_varlen64_h32_all_pairs():
     inp = workloads.make(workloads.PREFILL_VARLEN)
     note(f"[full] {inp.name} total={inp.total} min/max len={min(inp.lengths)}/{max(inp.lengths)}")
