@@ -284,3 +284,39 @@ def test_binding_rejects_mismatched_elementwise_tensors():
         kda.kda_short_conv(x, torch.zeros(128, 4))
     with pytest.raises(ValueError, match="cache_in: shape"):
         kda.kda_short_conv(x, torch.zeros(256, 4), cache_in=torch.zeros(1, 256, 4))
+
+
+def test_binding_calls_run_on_their_tensors_device(monkeypatch):
+    """Each binding call makes its tensors' GPU current first (the library launches on, and sizes
+    the prefill workspace for, the current device).  Checked on the host with a stand-in tensor
+    that reports cuda:1 and a recording stand-in for torch.cuda.device."""
+    import contextlib
+
+    from linear_attention_sequence_chunkwise_amd import kda
+
+    class OnCuda1(torch.Tensor):
+        @property
+        def is_cuda(self):
+            return True
+
+        @property
+        def device(self):
+            return torch.device("cuda", 1)
+
+    seen = []
+
+    @contextlib.contextmanager
+    def record(dev):
+        seen.append(dev)
+        yield
+
+    monkeypatch.setattr(torch.cuda, "device", record)
+
+    @kda._on_tensor_device
+    def call(a, b=None):
+        return "ran"
+
+    x = torch.zeros(2).as_subclass(OnCuda1)
+    assert call(torch.zeros(1), b=x) == "ran" and seen == [torch.device("cuda", 1)]
+    seen.clear()
+    assert call(torch.zeros(1)) == "ran" and seen == []  # no GPU tensor: no device switch
