@@ -87,11 +87,15 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
     const T* x = static_cast<const T*>(a.x);
     T* y = static_cast<T*>(a.y);
 
+    // With L2Norm the weights carry -log2(e): the convolution then yields Swish's exp2
+    // argument directly, and the normalisation, being scale-invariant (its epsilon scaled by
+    // log2(e)^2 and its sign flipped), removes the factor again
+    constexpr float kWs = L2 > 0 ? -kLog2e : 1.f;
     float wt[8][W];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int i = 0; i < W; ++i) wt[e][i] = live ? a.w[static_cast<int64_t>(c0 + e) * W + i] : 0.f;
+        for (int i = 0; i < W; ++i) wt[e][i] = live ? kWs * a.w[static_cast<int64_t>(c0 + e) * W + i] : 0.f;
 
     int n = seq_of(a.cu, a.n_seqs, a.T, tb);
     int64_t s0 = seq_start(a.cu, a.T, n), s1 = seq_start(a.cu, a.T, n + 1);
@@ -124,7 +128,10 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
             float acc = wt[e][HIST] * cur[e];
 #pragma unroll
             for (int i = 0; i < HIST; ++i) acc += wt[e][i] * win[i][e];
-            out[e] = acc * fast_rcp(1.f + fast_exp2(-acc * kLog2e));  // Swish
+            if constexpr (L2 > 0)
+                out[e] = acc * fast_rcp(1.f + fast_exp2(acc));  // -log2(e) Swish
+            else
+                out[e] = acc * fast_rcp(1.f + fast_exp2(-acc * kLog2e));  // Swish
             ss += out[e] * out[e];
         }
         if constexpr (L2 > 0) {
@@ -135,7 +142,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ShortConvArgs a) {
             ss += dpp_f32<0x4E>(ss);   // quad_perm [2,3,0,1]
             ss += dpp_f32<0x141>(ss);  // row_half_mirror
             if constexpr (L2 == 128) ss += dpp_f32<0x128>(ss);  // row_ror:8
-            const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
+            const float inv = -__builtin_amdgcn_rsqf(ss + 1e-6f * kLog2e * kLog2e);
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
