@@ -42,6 +42,12 @@ template <> struct Vec8<float> {
     }
 };
 
+// x of another lane of the same row of 16, chosen by a DPP control code
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 }  // namespace
 
 template <int DV, typename T>
@@ -81,8 +87,13 @@ __global__ void __launch_bounds__(256) output_gate_kernel(OutputGateArgs a) {
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss += x[u][i] * x[u][i];
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off);
+            // the row's LPR lanes are one DPP row (16) or half-row (8): quads, then the two
+            // quads of each half-row (mirror), then the two half-rows, all without LDS
+            static_assert(LPR == 8 || LPR == 16, "rows of 64 or 128 channels");
+            ss += dpp_f32<0xB1>(ss);   // quad_perm [1,0,3,2]
+            ss += dpp_f32<0x4E>(ss);   // quad_perm [2,3,0,1]
+            ss += dpp_f32<0x141>(ss);  // row_half_mirror
+            if constexpr (LPR == 16) ss += dpp_f32<0x128>(ss);  // row_ror:8
             const float inv = __builtin_amdgcn_rsqf(ss * (1.f / DV) + a.eps);
             float out[8];
 #pragma unroll
